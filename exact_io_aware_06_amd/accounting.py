@@ -1,0 +1,82 @@
+"""Algorithmic work and traffic of the attention path (host-side arithmetic).
+
+These counts price the kernels against the roofline. They are the useful
+work only: masked pairs inside boundary tiles, exponentials and other vector
+work are not counted as FLOPs, and re-reads served by caches are not counted
+as bytes.
+
+* Prefill: every visible (query, key) pair costs one d-long dot product for
+  Q K^T and one d-long multiply-add into the output for P V, i.e. 4 d FLOPs.
+  The full (non-causal, unwindowed) count 4 d N^2 is the O(n^2 d) cost of the
+  QK^T product the pages describe ("Chapter 3.1 - The Cost of Attention",
+  section 2; "Quadratic Complexity Bottleneck", compute entry).
+* Decode: the KV cache is read once per step ("Attention Research", section 1:
+  memory O(S), read every decode step), plus q in and O / LSE out.
+"""
+
+from __future__ import annotations
+
+
+def visible_pairs(Nq: int, Nk: int, causal: bool, window: int) -> int:
+    """Number of (query, key) pairs a single head attends over.
+
+    Query row i sits at position p = i + Nk - Nq. It sees keys j in
+    [lo, hi] with lo = max(0, p - W) if W > 0 else 0, and hi = p if causal,
+    else min(Nk - 1, p + W) if W > 0, else Nk - 1.
+    """
+    if Nq <= 0 or Nk <= 0:
+        return 0
+    total = 0
+    off = Nk - Nq
+    # Rows fall into a few linear regimes; summing per row keeps this obvious.
+    for i in range(Nq):
+        p = i + off
+        lo = max(0, p - window) if window > 0 else 0
+        if causal:
+            hi = min(Nk - 1, p)
+        elif window > 0:
+            hi = min(Nk - 1, p + window)
+        else:
+            hi = Nk - 1
+        if hi >= lo:
+            total += hi - lo + 1
+    return total
+
+
+def prefill_flops(B: int, H: int, Nq: int, Nk: int, d: int, causal: bool, window: int) -> int:
+    """Algorithmic FLOPs of one forward call: 4 d per visible pair per head."""
+    return 4 * d * visible_pairs(Nq, Nk, causal, window) * B * H
+
+
+def dense_attention_ops(n: int, d: int = 1) -> int:
+    """Multiply-adds of the full n x n score matrix QK^T: n^2 d."""
+    return n * n * d
+
+
+def score_matrix_bytes(n: int, bytes_per_elem: int = 4) -> int:
+    """Bytes of one head's materialised n x n score matrix."""
+    return n * n * bytes_per_elem
+
+
+def prefill_bytes(B, H, Hkv, Nq, Nk, d, elem_bytes=2, lse=True) -> int:
+    """Compulsory HBM bytes of one forward call: Q, K, V read once; O (+LSE) written."""
+    qo = 2 * B * H * Nq * d * elem_bytes
+    kv = 2 * B * Hkv * Nk * d * elem_bytes
+    return qo + kv + (B * H * Nq * 4 if lse else 0)
+
+
+def decode_bytes(B, H, Hkv, Nk, d, elem_bytes=2, window=0, lse=True) -> int:
+    """Compulsory HBM bytes of one decode step.
+
+    K and V are read once over the visible keys (all Nk, or the last W + 1
+    with a window); q is read and O (and LSE) written once.
+    """
+    keys = Nk if window <= 0 else min(Nk, window + 1)
+    kv = 2 * B * Hkv * keys * d * elem_bytes
+    qo = 2 * B * H * d * elem_bytes
+    return kv + qo + (B * H * 4 if lse else 0)
+
+
+def decode_flops(B, H, Nk, d, window=0) -> int:
+    keys = Nk if window <= 0 else min(Nk, window + 1)
+    return 4 * d * keys * B * H

@@ -1,0 +1,152 @@
+"""Workload shapes and seeded N(0,1) tensors for the attention path.
+
+Every tensor is drawn one batch index at a time from its own seeded torch
+generator, so any batch slice can be rebuilt alone (the decode cache at full
+size is 8.6 GB of bf16; rebuilding one sequence of it is 134 MB).
+
+Generation recipe, for tensor ``tid`` (q=0, k=1, v=2), batch index ``b``:
+
+* generator seeded with ``seed_key(seed, tid, b)`` on the requested device;
+* ``torch.randn`` in float32;
+* optional multiply by a float32 constant (the sharpened workload);
+* one round-to-nearest-even cast to the storage dtype (bf16 or fp32).
+
+The same seed on the same device type always yields the same bits. CPU and
+GPU generators are different streams: a test draws on one device and copies
+the tensors it needs to the other.
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+TID_Q, TID_K, TID_V = 0, 1, 2
+
+
+def seed_key(seed: int, tid: int, b: int) -> int:
+    """Generator seed for tensor ``tid``, batch index ``b`` of run ``seed``."""
+    return int(seed) * 10_000_000 + int(tid) * 100_000 + int(b)
+
+
+def _dtype(name: str) -> torch.dtype:
+    return {"bf16": torch.bfloat16, "f32": torch.float32}[name]
+
+
+def gen_normal(shape, seed: int, tid: int, b: int, dtype: str = "bf16",
+               mult: float = 1.0, device="cpu") -> torch.Tensor:
+    """One batch slice: N(0,1) float32, times ``mult`` in float32, then RNE cast."""
+    dev = torch.device(device)
+    g = torch.Generator(device=dev)
+    g.manual_seed(seed_key(seed, tid, b))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=dev)
+    if mult != 1.0:
+        x.mul_(float(np.float32(mult)))
+    return x.to(_dtype(dtype))
+
+
+@dataclass(frozen=True)
+class PrefillConfig:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str          # "bf16" or "f32"
+    causal: int
+    window: int
+    scale: float        # the value handed to the kernel (float32-representable)
+    qk_mult: float = 1.0  # applied to Q and K before the cast (sharpened logits)
+    note: str = ""
+
+    def with_(self, **kw) -> "PrefillConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return PrefillConfig(**d)
+
+
+@dataclass(frozen=True)
+class DecodeConfig:
+    name: str
+    B: int
+    H: int
+    Hkv: int
+    Nk: int
+    d: int
+    splits: int
+    scale: float
+    window: int = 0
+    dtype: str = "bf16"
+    note: str = ""
+
+    def with_(self, **kw) -> "DecodeConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return DecodeConfig(**d)
+
+
+def _f32(x: float) -> float:
+    return float(np.float32(x))
+
+
+# The five workloads. Shapes follow the contexts the pages discuss (2k-8k
+# training contexts, 32k documents, KV-cache decode); values are i.i.d. N(0,1).
+CONFIGS = {
+    "c1": PrefillConfig("c1", 1, 1, 1, 256, 256, 64, "f32", 0, 0, _f32(1 / 8),
+                        note="single head, non-causal, fp32"),
+    "c2": PrefillConfig("c2", 4, 16, 16, 2048, 2048, 64, "bf16", 1, 0, _f32(1 / 8),
+                        note="causal self-attention prefill"),
+    # Q and K are each multiplied by 3 * d^-1/4 before the bf16 cast, which folds
+    # the 1/sqrt(d) into the inputs and sharpens the logits threefold; the kernel
+    # scale is therefore 1.0.
+    "c3": PrefillConfig("c3", 1, 32, 8, 8192, 8192, 128, "bf16", 1, 0, 1.0,
+                        qk_mult=3.0 * 128 ** -0.25,
+                        note="causal GQA prefill, sharpened logits"),
+    "c4": PrefillConfig("c4", 1, 32, 8, 32768, 32768, 128, "bf16", 1, 4096,
+                        _f32(1 / math.sqrt(128)),
+                        note="causal sliding-window GQA prefill"),
+    "c5": DecodeConfig("c5", 64, 32, 8, 32768, 128, 16, _f32(1 / math.sqrt(128)),
+                       note="split-K decode over a 32k KV cache"),
+}
+
+
+def prefill_inputs(cfg: PrefillConfig, seed: int, device="cpu", batches=None):
+    """(q, k, v) for a prefill config: q [B,H,Nq,d], k/v [B,Hkv,Nk,d].
+
+    ``batches`` restricts generation to a list of batch indices (the result
+    then has len(batches) rows in dim 0).
+    """
+    bs = range(cfg.B) if batches is None else list(batches)
+    qs, ks, vs = [], [], []
+    for b in bs:
+        qs.append(gen_normal((cfg.H, cfg.Nq, cfg.d), seed, TID_Q, b, cfg.dtype,
+                             cfg.qk_mult, device))
+        ks.append(gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_K, b, cfg.dtype,
+                             cfg.qk_mult, device))
+        vs.append(gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_V, b, cfg.dtype,
+                             1.0, device))
+    return torch.stack(qs), torch.stack(ks), torch.stack(vs)
+
+
+def decode_inputs(cfg: DecodeConfig, seed: int, device="cpu", batches=None):
+    """(q, k_cache, v_cache) for decode: q [B,H,d], caches [B,Hkv,Nk,d].
+
+    The caches are filled in place one sequence at a time so peak host memory
+    stays at one sequence of float32 on top of the bf16 result.
+    """
+    bs = range(cfg.B) if batches is None else list(batches)
+    n = len(bs)
+    dt = _dtype(cfg.dtype)
+    q = torch.empty((n, cfg.H, cfg.d), dtype=dt, device=device)
+    kc = torch.empty((n, cfg.Hkv, cfg.Nk, cfg.d), dtype=dt, device=device)
+    vc = torch.empty_like(kc)
+    for i, b in enumerate(bs):
+        q[i] = gen_normal((cfg.H, cfg.d), seed, TID_Q, b, cfg.dtype, 1.0, device)
+        kc[i] = gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_K, b, cfg.dtype, 1.0, device)
+        vc[i] = gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_V, b, cfg.dtype, 1.0, device)
+    return q, kc, vc
