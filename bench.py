@@ -1,0 +1,236 @@
+"""Benchmark of the fused-attention hot path on one MI355X.
+
+One step = the whole path once over resident synthetic inputs:
+  * causal GQA prefill, B=1 H=32 Hkv=8 N=8192 d=128, bf16 (sharpened Q/K);
+  * split-K decode, B=64 H=32 Hkv=8 Nk=32768 d=128, bf16, 16 splits + merge;
+  * fp32 single-head forward, N=256 d=64 (the fp32 variant).
+The headline value is the prefill's algorithmic TFLOP/s (4 d per visible
+query-key pair); the decode's algorithmic GB/s (K/V cache read once + q + O +
+LSE) is reported beside it. Kernel durations come from HIP events recorded on
+the stream the kernels are launched on, around each call inside the timed
+steps.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "attention fwd TFLOP/s (% bf16 MFMA peak) at N=8k d=128; decode GB/s (% HBM)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "fwd_bf16": ["exact_io_aware_06_amd/csrc/fwd_bf16.hip", "exact_io_aware_06_amd/csrc/common.hpp"],
+    "decode": ["exact_io_aware_06_amd/csrc/decode.hip", "exact_io_aware_06_amd/csrc/common.hpp"],
+}
+
+
+def source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kind: str):
+    """Counter-derived HBM bytes per launch, if measured on this exact source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f).get(kind)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_digest") != source_digest(kind):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline_prefill(cfg, heads: int):
+    """The oracle, untuned, on `heads` heads of the prefill workload."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+    from exact_io_aware_06_amd import accounting
+
+    sub = cfg.with_(H=heads, Hkv=max(1, heads * cfg.Hkv // cfg.H))
+    q, k, v = synth.prefill_inputs(sub, seed=0)
+    q64 = q.double().numpy()
+    k64, v64 = k.double().numpy(), v.double().numpy()
+    t0 = time.perf_counter()
+    oracle.attention_ref(q64, k64, v64, sub.scale, sub.causal, sub.window)
+    dt = time.perf_counter() - t0
+    flops = accounting.prefill_flops(1, heads, sub.Nq, sub.Nk, sub.d, sub.causal, sub.window)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{heads} of {cfg.H} heads of the prefill workload (fp64, full score "
+                      f"matrix per head), {dt:.2f} s wall",
+            "seconds": dt}
+
+
+def cpu_baseline_decode(cfg, seqs: int):
+    import torch
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import synth
+    from exact_io_aware_06_amd import accounting
+
+    sub = cfg.with_(B=seqs)
+    q, kc, vc = synth.decode_inputs(sub, seed=0)
+    t0 = time.perf_counter()
+    oracle.decode_ref(q, kc, vc, sub.scale, sub.window)
+    dt = time.perf_counter() - t0
+    nbytes = accounting.decode_bytes(seqs, sub.H, sub.Hkv, sub.Nk, sub.d, window=sub.window)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{seqs} of {cfg.B} sequences of the decode workload, {dt:.2f} s wall",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=2)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(each GPU's share of prefill or decode is the single-GPU workload).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import synth
+    import exact_io_aware_06_amd as mi
+    from exact_io_aware_06_amd import accounting
+
+    if not os.path.exists(mi.library_path()):
+        from exact_io_aware_06_amd import build
+        build.build()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    cp = synth.CONFIGS["c3"]
+    cd = synth.CONFIGS["c5"]
+    cf = synth.CONFIGS["c1"]
+    q, k, v = synth.prefill_inputs(cp, seed=0, device=dev)
+    qd, kc, vc = synth.decode_inputs(cd, seed=0, device=dev)
+    qf, kf, vf = synth.prefill_inputs(cf, seed=0, device=dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(cp.B, cp.H, cp.Nq, dtype=torch.float32, device=dev)
+    od = torch.empty_like(qd)
+    lsed = torch.empty(cd.B, cd.H, dtype=torch.float32, device=dev)
+    ws = torch.empty(mi.decode_workspace_bytes(cd.B, cd.H, cd.Hkv, cd.Nk, cd.d, cd.splits),
+                     dtype=torch.uint8, device=dev)
+    of = torch.empty_like(qf)
+    lsef = torch.empty(cf.B, cf.H, cf.Nq, dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal, window=cp.window, out=o, lse=lse)
+        if ev is not None:
+            ev[1].record()
+        mi.attn_decode(qd, kc, vc, scale=cd.scale, window=cd.window, num_splits=cd.splits,
+                       out=od, lse=lsed, workspace=ws)
+        if ev is not None:
+            ev[2].record()
+        mi.attn_fwd(qf, kf, vf, scale=cf.scale, causal=cf.causal, window=cf.window, out=of,
+                    lse=lsef)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
+    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
+    f32_ms = [e[2].elapsed_time(e[3]) for e in events]
+    mean = lambda xs: sum(xs) / len(xs)
+
+    pre_flops = accounting.prefill_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
+    dec_bytes = accounting.decode_bytes(cd.B, cd.H, cd.Hkv, cd.Nk, cd.d, window=cd.window)
+    f32_flops = accounting.prefill_flops(cf.B, cf.H, cf.Nq, cf.Nk, cf.d, cf.causal, cf.window)
+    pre_tflops = pre_flops / (mean(pre_ms) * 1e-3) / 1e12
+    dec_gbs = dec_bytes / (mean(dec_ms) * 1e-3) / 1e9
+
+    out = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded i.i.d. N(0,1) (prefill Q and K times 3*d^-1/4 before the bf16 cast)",
+        "config": {
+            "workload": "causal GQA prefill B1 H32 Hkv8 N8192 d128 bf16 (sharpened, scale 1.0) "
+                        "+ split-K decode B64 H32 Hkv8 Nk32768 d128 bf16 16 splits "
+                        "+ fp32 forward B1 H1 N256 d64",
+            "prefill": {"B": cp.B, "H": cp.H, "Hkv": cp.Hkv, "N": cp.Nq, "d": cp.d,
+                        "causal": cp.causal, "window": cp.window, "scale": cp.scale,
+                        "algorithmic_flops": pre_flops},
+            "decode": {"B": cd.B, "H": cd.H, "Hkv": cd.Hkv, "Nk": cd.Nk, "d": cd.d,
+                       "splits": cd.splits, "algorithmic_bytes": dec_bytes},
+        },
+        "prefill_ms": round(mean(pre_ms), 4),
+        "prefill_ms_min": round(min(pre_ms), 4),
+        "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(mean(dec_ms), 4),
+                   "ms_min": round(min(dec_ms), 4), "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
+        "fp32_forward": {"ms": round(mean(f32_ms), 4),
+                         "tflops": round(f32_flops / (mean(f32_ms) * 1e-3) / 1e12, 3)},
+        "roofline": {"kernel": "fwd_bf16_kernel<128>", "bound": "mfma",
+                     "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic_for("fwd_bf16")},
+        "roofline_decode": {"kernel": "decode_split_kernel<128> + decode_merge_kernel<128>",
+                            "bound": "hbm", "achieved": round(dec_gbs, 1),
+                            "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                            "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
+                            "traffic": traffic_for("decode")},
+    }
+    del kc, vc
+    torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        cb = cpu_baseline_prefill(cp, args.cpu_heads)
+        out["cpu_baseline"] = {kk: (round(vv, 6) if isinstance(vv, float) else vv)
+                               for kk, vv in cb.items() if kk != "seconds"}
+        cbd = cpu_baseline_decode(cd, args.cpu_seqs)
+        out["cpu_baseline_decode"] = {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                                      for kk, vv in cbd.items() if kk != "seconds"}
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

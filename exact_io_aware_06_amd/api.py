@@ -1,0 +1,192 @@
+"""ctypes binding of libmiattn (argument marshalling only).
+
+Every step of the computation runs in the HIP library. This module checks
+tensor dtype/device/shape/contiguity, allocates outputs with torch, and
+passes raw pointers plus the current torch stream. If the library is not
+built, the first call raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import threading
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libmiattn.so"
+_lock = threading.Lock()
+_lib = None
+
+MIATTN_OK = 0
+
+
+class MiattnError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"libmiattn status {status}: {msg}")
+        self.status = status
+
+
+def library_path() -> str:
+    return os.environ.get("MIATTN_LIBRARY", os.path.join(_HERE, _LIB_NAME))
+
+
+def load_library():
+    """Load libmiattn.so (once) and declare the C signatures."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+                "from the repository root")
+        lib = ctypes.CDLL(path)
+        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        fwd_args = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+        lib.attn_fwd.argtypes = fwd_args
+        lib.attn_fwd.restype = I
+        lib.attn_fwd_f32.argtypes = fwd_args
+        lib.attn_fwd_f32.restype = I
+        lib.attn_fwd_tile_counts.argtypes = fwd_args[:-1] + [P, P]
+        lib.attn_fwd_tile_counts.restype = I
+        lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+        lib.attn_fwd_tile_shape.restype = I
+        lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        lib.attn_decode_workspace_bytes.restype = S
+        lib.attn_decode_num_splits.argtypes = [I, I, I, I]
+        lib.attn_decode_num_splits.restype = I
+        lib.attn_decode_splitk.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+        lib.attn_decode_splitk.restype = I
+        lib.attn_strerror.argtypes = [I]
+        lib.attn_strerror.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _check(status: int):
+    if status != MIATTN_OK:
+        msg = load_library().attn_strerror(status).decode()
+        raise MiattnError(status, msg)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr() if t is not None and t.numel() > 0 else 0)
+
+
+def _stream(device):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require(cond, msg):
+    if not cond:
+        raise ValueError(msg)
+
+
+def fwd_tile_shape(d: int, is_f32: bool = False):
+    lib = load_library()
+    bm, bn = ctypes.c_int(), ctypes.c_int()
+    _check(lib.attn_fwd_tile_shape(int(d), int(bool(is_f32)), ctypes.byref(bm), ctypes.byref(bn)))
+    return bm.value, bn.value
+
+
+def _fwd_checks(q, k, v):
+    import torch
+    _require(q.dim() == 4 and k.dim() == 4 and v.dim() == 4, "q, k, v must be 4-D")
+    _require(q.is_cuda and k.device == q.device and v.device == q.device,
+             "q, k, v must be on the same GPU")
+    _require(q.dtype in (torch.bfloat16, torch.float32), "dtype must be bfloat16 or float32")
+    _require(k.dtype == q.dtype and v.dtype == q.dtype, "q, k, v dtypes differ")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
+             "q, k, v must be contiguous")
+    B, H, Nq, d = q.shape
+    _require(k.shape[0] == B and k.shape[3] == d and v.shape == k.shape,
+             "k/v must be [B, Hkv, Nk, d] matching q")
+    return B, H, k.shape[1], Nq, k.shape[2], d
+
+
+def attn_fwd(q, k, v, scale=None, causal=False, window=0, out=None, lse=None):
+    """Fused attention forward. Returns (O [B,H,Nq,d] like q, LSE [B,H,Nq] fp32).
+
+    bf16 inputs run the bf16 matrix-core kernel, fp32 inputs the fp32 kernel.
+    """
+    import torch
+    B, H, Hkv, Nq, Nk, d = _fwd_checks(q, k, v)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    _require(lse.shape == (B, H, Nq) and lse.dtype == torch.float32 and lse.is_contiguous(),
+             "bad lse")
+    lib = load_library()
+    fn = lib.attn_fwd if q.dtype == torch.bfloat16 else lib.attn_fwd_f32
+    with torch.cuda.device(q.device):
+        _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d,
+                  ctypes.c_float(scale), int(bool(causal)), int(window), _stream(q.device)))
+    return out, lse
+
+
+def fwd_tile_counts(q, k, v, scale=None, causal=False, window=0):
+    """attn_fwd (bf16) plus per-work-group (tiles loaded, tiles masked) counts.
+
+    Returns (O, LSE, counts [B, H, ceil(Nq/BM), 2] int32).
+    """
+    import torch
+    B, H, Hkv, Nq, Nk, d = _fwd_checks(q, k, v)
+    _require(q.dtype == torch.bfloat16, "tile counts are for the bf16 kernel")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    bm, _ = fwd_tile_shape(d, False)
+    nqt = -(-Nq // bm)
+    out = torch.empty_like(q)
+    lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    counts = torch.full((B, H, nqt, 2), -1, dtype=torch.int32, device=q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.attn_fwd_tile_counts(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                        B, H, Hkv, Nq, Nk, d, ctypes.c_float(scale),
+                                        int(bool(causal)), int(window), _ptr(counts),
+                                        _stream(q.device)))
+    return out, lse, counts
+
+
+def decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits=0) -> int:
+    return int(load_library().attn_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits))
+
+
+def attn_decode(q, k_cache, v_cache, scale=None, window=0, num_splits=0,
+                out=None, lse=None, workspace=None):
+    """Split-K decode. q [B,H,d] bf16, caches [B,Hkv,Nk,d] bf16.
+
+    Returns (O [B,H,d] bf16, LSE [B,H] fp32).
+    """
+    import torch
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
+             "q [B,H,d], caches [B,Hkv,Nk,d]")
+    _require(q.is_cuda and k_cache.device == q.device and v_cache.device == q.device,
+             "tensors must be on the same GPU")
+    _require(q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16
+             and v_cache.dtype == torch.bfloat16, "decode takes bfloat16")
+    _require(q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous(),
+             "tensors must be contiguous")
+    B, H, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    _require(k_cache.shape[0] == B and k_cache.shape[3] == d, "cache shape mismatch")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    nbytes = int(lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                      _ptr(lse), B, H, Hkv, Nk, d, ctypes.c_float(scale),
+                                      int(window), int(num_splits), _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+    return out, lse

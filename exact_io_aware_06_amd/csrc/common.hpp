@@ -1,0 +1,101 @@
+// Device helpers shared by the libmiattn kernels (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace miattn {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr float kInf = __builtin_huge_valf();
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 16-byte global load that yields zeros when `ok` is false.
+__device__ __forceinline__ uint4 load16(const uint16_t* p, bool ok) {
+  uint4 r = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) r = *reinterpret_cast<const uint4*>(p);
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ bf16x8 lds_read_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const uint4*>(p));
+}
+
+// D += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate. Lane l holds
+// A[l % 32][8 (l / 32) .. +8] and B[8 (l / 32) .. +8][l % 32]; D[i][j] sits in
+// lane j + 32 * ((i / 4) % 2), register 4 (i / 8) + i % 4.
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Pad between the last MFMA of a block and the first vector-ALU read of its
+// result. With fp32 accumulators in arch VGPRs, this toolchain was seen to
+// leave too few wait states after v_mfma_f32_32x32x16_bf16 on some control
+// paths, so stale accumulator values were read back (wrong, run-to-run varying
+// results). 24 explicit wait states, fenced against rescheduling, remove that
+// and cost ~24 issue cycles per block, during which other waves issue.
+__device__ __forceinline__ void mfma_drain() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+// Value of `x` in the lane 32 positions away (the other half of the wave).
+__device__ __forceinline__ float swap_halves(float x) {
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ bool wave_any(bool pred) {
+  return __builtin_amdgcn_ballot_w64(pred) != 0;
+}
+
+// Eight fp32 values to bf16, round to nearest even.
+__device__ __forceinline__ bf16x8 to_bf16x8(const f32x8 v) {
+  return __builtin_convertvector(v, bf16x8);
+}
+
+// Pairwise sum of eight fp32 values.
+__device__ __forceinline__ float sum_f32x8(const f32x8 v) {
+  return ((v[0] + v[1]) + (v[2] + v[3])) + ((v[4] + v[5]) + (v[6] + v[7]));
+}
+
+// Sum of the eight bf16 values in `v`, added to `acc` in fp32 (packed bf16
+// dot products against (1, 1); the products are exact).
+__device__ __forceinline__ float sum_bf16x8(bf16x8 v, float acc) {
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  const b2 one = {(__bf16)1.0f, (__bf16)1.0f};
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 4, 5), one, acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(v, v, 6, 7), one, acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+  f2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// Interleave the low halves (pick = 0) or high halves (pick = 1) of two
+// dwords holding bf16 pairs: result = {a.half, b.half}.
+__device__ __forceinline__ uint32_t interleave16(uint32_t a, uint32_t b, int pick) {
+  return pick ? ((a >> 16) | (b & 0xffff0000u)) : ((a & 0xffffu) | (b << 16));
+}
+
+__device__ __forceinline__ uint32_t u4_get(const uint4& u, int i) {
+  return i == 0 ? u.x : i == 1 ? u.y : i == 2 ? u.z : u.w;
+}
+
+}  // namespace miattn

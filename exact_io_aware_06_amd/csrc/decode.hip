@@ -1,0 +1,333 @@
+// Split-K decode (one query token per sequence against a KV cache) and the
+// log-sum-exp merge of its partial results, gfx950.
+//
+// Decode is bound by reading the KV cache once per step ("Attention
+// Research", section 1; "Quadratic Complexity Bottleneck", KV cache entry).
+// Split-K over keys ("Attention Research", section 2) gives the GPU enough
+// independent work: the key range of each sequence is cut into S contiguous
+// chunks, and each (sequence, KV head, chunk) becomes one work-group that
+// reads its K/V rows exactly once for all G query heads sharing that KV head.
+//
+// Split kernel: the work-group walks its chunk in tiles of 128 keys staged
+// through LDS (K as rows, V transposed, as in the prefill kernel); wave w
+// takes keys [32w, 32w + 32) of each tile and treats the G query heads as the
+// 32 columns of a transposed score tile S^T = K Q^T (columns >= G are zero
+// and discarded). Each wave keeps its own running max / sum / output; at the
+// end the four waves are combined through LDS into one normalised partial
+// O_s and its lse_s = ln sum exp(scores) for the chunk.
+//
+// Merge kernel: per (sequence, query head), LSE = ln sum_s exp(lse_s) and
+// O = sum_s exp(lse_s - LSE) O_s; chunks with no visible key have
+// lse_s = -inf and weigh nothing.
+
+#include <algorithm>
+#include <cstdio>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace miattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBN = 128;  // keys per tile: four waves x 32
+constexpr float kRescaleThreshold = 8.0f;
+
+struct SplitParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  float* o_s;
+  float* lse_s;
+  int B, H, Hkv, Nk, G, S, C;
+  int vis_lo;  // first visible key (window), else 0
+  float scale, scale_log2, thr_raw;
+};
+
+struct MergeParams {
+  const float* o_s;
+  const float* lse_s;
+  uint16_t* o;
+  float* lse;
+  int BH, S;
+};
+
+template <int D>
+struct DTile {
+  static constexpr int KSTR = D + 8;
+  static constexpr int VSTR = kBN + 8;
+  static constexpr int STAGE = kBN * KSTR + D * VSTR;
+  static constexpr int DB = D / 32;
+  static constexpr int KS = D / 16;
+  static constexpr int DCH = D / 8;
+  static constexpr int KCH = kBN / 4;
+  static constexpr int NB = KCH * DCH / kThreads;  // 4x8 blocks per thread per tile
+  static_assert(NB * kThreads == KCH * DCH, "tile blocks must split evenly");
+  // The end-of-chunk combine reuses the tile storage.
+  static_assert((4 * 32 * D + 3 * 4 * 32) * 4 <= STAGE * 2, "combine scratch fits");
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p) {
+  using T = DTile<D>;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+  const int s = blockIdx.x % p.S;
+  const int bk = blockIdx.x / p.S;
+  const int kvh = bk % p.Hkv, b = bk / p.Hkv;
+
+  const int lo = min(p.Nk, s * p.C);
+  const int hi = min(p.Nk, lo + p.C);
+  const int start = max(lo, p.vis_lo);
+  const int ntiles = hi > start ? (hi - start + kBN - 1) / kBN : 0;
+
+  // Query heads of this group as the B-operand columns.
+  const bool qvalid = l32 < p.G;
+  const int hq = kvh * p.G + (qvalid ? l32 : 0);
+  bf16x8 qf[T::KS];
+  {
+    const uint16_t* qp = p.q + ((size_t)b * p.H + hq) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qp + ks * 16, qvalid));
+  }
+
+  const size_t head_kv = ((size_t)b * p.Hkv + kvh) * p.Nk;
+  const uint16_t* kbase = p.k + head_kv * D;
+  const uint16_t* vbase = p.v + head_kv * D;
+
+  uint4 kreg[T::NB][4], vreg[T::NB][4];
+  auto load_tile = [&](int t0) {
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb) {
+      const int bi = tid + nb * kThreads;
+      const int kc_k = bi / T::DCH, dc_k = bi % T::DCH;
+      const int kc_v = bi % T::KCH, dc_v = bi / T::KCH;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int rk = t0 + kc_k * 4 + r;
+        kreg[nb][r] = load16(kbase + (size_t)(rk < hi ? rk : 0) * D + dc_k * 8, rk < hi);
+        const int rv = t0 + kc_v * 4 + r;
+        vreg[nb][r] = load16(vbase + (size_t)(rv < hi ? rv : 0) * D + dc_v * 8, rv < hi);
+      }
+    }
+  };
+  auto store_tile = [&]() {
+    uint16_t* ks = smem;
+    uint16_t* vs = smem + kBN * T::KSTR;
+#pragma unroll
+    for (int nb = 0; nb < T::NB; ++nb) {
+      const int bi = tid + nb * kThreads;
+      const int kc_k = bi / T::DCH, dc_k = bi % T::DCH;
+      const int kc_v = bi % T::KCH, dc_v = bi / T::KCH;
+      const int vpos = (kc_v >> 2) * 16 + (((kc_v & 1) << 1) | ((kc_v >> 1) & 1)) * 4;
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *reinterpret_cast<uint4*>(ks + (kc_k * 4 + r) * T::KSTR + dc_k * 8) = kreg[nb][r];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int w = e >> 1, half = e & 1;
+        uint2 col;
+        col.x = interleave16(u4_get(vreg[nb][0], w), u4_get(vreg[nb][1], w), half);
+        col.y = interleave16(u4_get(vreg[nb][2], w), u4_get(vreg[nb][3], w), half);
+        *reinterpret_cast<uint2*>(vs + (dc_v * 8 + e) * T::VSTR + vpos) = col;
+      }
+    }
+  };
+
+  f32x16 oacc[T::DB];
+#pragma unroll
+  for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
+  float m_ref = -kInf;
+  float l_b = 0.f, l_f = 0.f;  // row sums of the bf16-rounded and the fp32 P
+
+  if (ntiles > 0) load_tile(start);
+  for (int it = 0; it < ntiles; ++it) {
+    const int t0 = start + it * kBN;
+    __syncthreads();  // every wave is done with the previous tile
+    store_tile();
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(t0 + kBN);
+
+    const uint16_t* ks = smem;
+    const uint16_t* vs = smem + kBN * T::KSTR;
+    f32x16 sacc = f32x16{};
+    {
+      const uint16_t* kp = ks + (wave * 32 + l32) * T::KSTR + g * 8;
+#pragma unroll
+      for (int st = 0; st < T::KS; ++st) sacc = mfma32x32x16(lds_read_bf16x8(kp + st * 16), qf[st], sacc);
+    }
+    mfma_drain();
+    if (t0 + kBN > hi) {
+      const int lim = hi - (t0 + wave * 32 + 4 * g);  // offsets >= lim are past the chunk
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        sacc[r] = c < lim ? sacc[r] : -kInf;
+      }
+    }
+    float mx = -kInf;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_ref, mx);
+    const bool need = m_new > m_ref + p.thr_raw;
+    if (wave_any(need)) {
+      const float alpha = need ? fast_exp2((m_ref - m_new) * p.scale_log2) : 1.f;
+      if (need) m_ref = m_new;
+      l_b *= alpha;
+      l_f *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::DB; ++i) oacc[i] *= alpha;
+    }
+    const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
+    bf16x8 pf[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x8 pv;
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        pv[i] = fast_exp2(__builtin_fmaf(sacc[hf * 8 + i], p.scale_log2, -msub));
+      l_f += sum_f32x8(pv);
+      pf[hf] = to_bf16x8(pv);
+      l_b = sum_bf16x8(pf[hf], l_b);
+    }
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const uint16_t* vp = vs + (db * 32 + l32) * T::VSTR + wave * 32 + g * 8;
+#pragma unroll
+      for (int t = 0; t < 2; ++t) oacc[db] = mfma32x32x16(lds_read_bf16x8(vp + t * 16), pf[t], oacc[db]);
+    }
+    mfma_drain();
+  }
+
+  // Combine the four waves' (max, sum, un-normalised output) per head.
+  const float lb_col = l_b + swap_halves(l_b);
+  const float lf_col = l_f + swap_halves(l_f);
+  __syncthreads();  // tile storage is free again
+  float* ow = reinterpret_cast<float*>(smem);   // [4][32][D]
+  float* mw = ow + 4 * 32 * D;                  // [4][32]
+  float* lbw = mw + 4 * 32;                     // [4][32] sums of rounded P
+  float* lfw = lbw + 4 * 32;                    // [4][32] sums of fp32 P
+  if (qvalid) {
+    float* dst = ow + (wave * 32 + l32) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+        *reinterpret_cast<f32x4*>(dst + db * 32 + rr * 8) =
+            f32x4{oacc[db][rr * 4], oacc[db][rr * 4 + 1], oacc[db][rr * 4 + 2], oacc[db][rr * 4 + 3]};
+    if (g == 0) {
+      mw[wave * 32 + l32] = m_ref;
+      lbw[wave * 32 + l32] = lb_col;
+      lfw[wave * 32 + l32] = lf_col;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < p.G * D; idx += kThreads) {
+    const int col = idx / D, dim = idx - col * D;
+    float M = -kInf;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, mw[w * 32 + col]);
+    float Lb = 0.f, Lf = 0.f, acc = 0.f;
+    if (M != -kInf) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float mwv = mw[w * 32 + col];
+        const float e = mwv == -kInf ? 0.f : fast_exp2((mwv - M) * p.scale_log2);
+        Lb += e * lbw[w * 32 + col];
+        Lf += e * lfw[w * 32 + col];
+        acc += e * ow[(w * 32 + col) * D + dim];
+      }
+    }
+    const size_t row = ((size_t)b * p.H + kvh * p.G + col) * p.S + s;
+    p.o_s[row * D + dim] = Lb > 0.f ? acc / Lb : 0.f;
+    if (dim == 0) p.lse_s[row] = Lf > 0.f ? M * p.scale + fast_log2(Lf) * kLn2 : -kInf;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
+  constexpr int DPL = D / 64;  // dims per lane
+  const int lane = threadIdx.x;
+  const int bh = blockIdx.x;
+  const float* ls = p.lse_s + (size_t)bh * p.S;
+  const float* os = p.o_s + (size_t)bh * p.S * D;
+  float M = -kInf;
+  for (int s = lane; s < p.S; s += 64) M = fmaxf(M, ls[s]);
+#pragma unroll
+  for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w, 64));
+  float L = 0.f, acc[DPL];
+#pragma unroll
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
+  if (M != -kInf) {
+    for (int s = 0; s < p.S; ++s) {
+      const float lv = ls[s];
+      const float w = lv == -kInf ? 0.f : expf(lv - M);
+      L += w;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(w, os[(size_t)s * D + lane * DPL + i], acc[i]);
+    }
+  }
+  const float inv = L > 0.f ? 1.f / L : 0.f;
+  uint16_t* op = p.o + (size_t)bh * D + lane * DPL;
+  if (DPL == 2) {
+    *reinterpret_cast<uint32_t*>(op) = pack_bf16x2(acc[0] * inv, acc[DPL - 1] * inv);
+  } else {
+    const uint32_t w = pack_bf16x2(acc[0] * inv, 0.f);
+    *op = (uint16_t)(w & 0xffffu);
+  }
+  if (lane == 0 && p.lse != nullptr) p.lse[bh] = L > 0.f ? M + logf(L) : -kInf;
+}
+
+}  // namespace
+
+size_t decode_workspace_bytes(int B, int H, int d, int splits) {
+  return (size_t)B * H * splits * (size_t)(d + 1) * sizeof(float);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+  SplitParams sp;
+  sp.q = static_cast<const uint16_t*>(a.q);
+  sp.k = static_cast<const uint16_t*>(a.k);
+  sp.v = static_cast<const uint16_t*>(a.v);
+  sp.o_s = static_cast<float*>(a.workspace);
+  sp.lse_s = sp.o_s + (size_t)a.B * a.H * a.splits * a.d;
+  sp.B = a.B;
+  sp.H = a.H;
+  sp.Hkv = a.Hkv;
+  sp.Nk = a.Nk;
+  sp.G = a.H / a.Hkv;
+  sp.S = a.splits;
+  sp.C = (a.Nk + a.splits - 1) / a.splits;
+  sp.vis_lo = a.window > 0 ? (int)std::max(0LL, (long long)a.Nk - 1 - a.window) : 0;
+  sp.scale = a.scale;
+  sp.scale_log2 = a.scale * kLog2e;
+  sp.thr_raw = kRescaleThreshold / sp.scale_log2;
+  const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * a.splits);
+  if (log_enabled())
+    fprintf(stderr, "[miattn] decode d=%d splits=%d chunk=%d split_grid=%u merge_grid=%d\n", a.d,
+            a.splits, sp.C, nsplit_blk, a.B * a.H);
+  void* sargs[] = {&sp};
+  const void* sfn = a.d == 128 ? reinterpret_cast<const void*>(&decode_split_kernel<128>)
+                               : reinterpret_cast<const void*>(&decode_split_kernel<64>);
+  hipError_t e = hipLaunchKernel(sfn, dim3(nsplit_blk), dim3(kThreads), sargs, 0, stream);
+  if (e != hipSuccess) return e;
+
+  MergeParams mp;
+  mp.o_s = sp.o_s;
+  mp.lse_s = sp.lse_s;
+  mp.o = static_cast<uint16_t*>(a.o);
+  mp.lse = a.lse;
+  mp.BH = a.B * a.H;
+  mp.S = a.splits;
+  void* margs[] = {&mp};
+  const void* mfn = a.d == 128 ? reinterpret_cast<const void*>(&decode_merge_kernel<128>)
+                               : reinterpret_cast<const void*>(&decode_merge_kernel<64>);
+  return hipLaunchKernel(mfn, dim3((unsigned)mp.BH), dim3(64), margs, 0, stream);
+}
+
+}  // namespace miattn

@@ -1,0 +1,368 @@
+// Fused attention forward, bf16 in / bf16 out, fp32 accumulation, gfx950.
+//
+// One work-group owns BM = 128 query rows of one (batch, head); each of its
+// four waves owns 32 of those rows. The work-group streams the K/V tiles its
+// rows can see through LDS and keeps everything else in registers: the
+// score tile, the running row maximum and sum, and the output accumulator.
+// Nothing of size Nq x Nk is ever written to device memory ("Quadratic
+// Complexity Bottleneck", FlashAttention entry; grasp.study
+// efficient-attention lesson, "Tiling and Kernel Fusion", "Online Softmax").
+//
+// Matrix-core formulation. With v_mfma_f32_32x32x16_bf16 a lane holds one
+// column of the 32x32 result. The kernel therefore computes the transposed
+// score tile S^T = K Q^T (keys as rows, this wave's 32 queries as columns):
+// each lane then holds 16 keys of ONE query row, and the other 16 keys of
+// that row sit in the lane 32 apart. The row max and row sum are in-lane
+// reductions plus a single exchange between the two wave halves. The same
+// registers, rounded to bf16, are directly the B operand of O^T += V^T P^T,
+// so P never leaves the registers. V is staged into LDS transposed (dims as
+// rows) with the key order the P registers imply, so each lane reads its V^T
+// operand with one 16-byte LDS read.
+//
+// Online softmax (the pages' running max and running denominator, rescaling
+// the partial output when the maximum grows) is done lazily: the reference
+// maximum used for the exponentials is only moved when a row's new maximum
+// exceeds it by more than 2^8 in the exp2 domain. The final O / l and
+// LSE = m + ln l are identical in exact arithmetic for any reference value;
+// bounding the growth keeps P <= 256, far from fp32/bf16 overflow, and skips
+// most of the rescaling multiplies.
+//
+// Work decomposition: grid = B * H * ceil(Nq / BM) work-groups, the query
+// tiles with the most visible keys first (causal), and when (B * Hkv) is a
+// multiple of 8 the work-groups of one K/V head are kept on one XCD (one L2)
+// by undoing the round-robin dispatch of consecutive work-group ids across the
+// eight XCDs. Key tiles that the causal or window mask hides from every row
+// of the work-group are never loaded; only tiles that straddle a mask edge
+// (or the end of the keys) evaluate the mask per element.
+
+#include <cstdio>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace miattn {
+
+namespace {
+
+constexpr int kBM = 128;
+constexpr int kThreads = 256;
+// exp2-domain head-room before the reference maximum is moved.
+constexpr float kRescaleThreshold = 8.0f;
+
+struct FwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* o;
+  float* lse;
+  int B, H, Hkv, Nq, Nk, G;
+  float scale;       // softmax scale on q.k
+  float scale_log2;  // scale * log2(e)
+  float thr_raw;     // kRescaleThreshold / scale_log2, in q.k units
+  int causal, window;
+  int nqt;
+  int xcd_remap;
+  int* counts;
+};
+
+template <int D>
+struct Tile {
+  static constexpr int BN = (D == 128) ? 64 : 128;  // keys per K/V tile
+  static constexpr int KSTR = D + 8;                 // K row stride in LDS (elements)
+  static constexpr int VSTR = BN + 8;                // V^T row stride in LDS (elements)
+  static constexpr int STAGE = BN * KSTR + D * VSTR; // elements per LDS stage
+  static constexpr int KB = BN / 32;                 // 32-key blocks per tile
+  static constexpr int DB = D / 32;                  // 32-dim blocks of O
+  static constexpr int KS = D / 16;                  // k-steps of Q K^T
+  static constexpr int PS = BN / 16;                 // k-steps of P V
+  static constexpr int DCH = D / 8;                  // 8-element chunks per row
+  static constexpr int KCH = BN / 4;                 // 4-key chunks per tile
+  static_assert(KCH * DCH == kThreads, "one 4x8 block per thread per tile");
+};
+
+__device__ __forceinline__ void decode_workgroup(const FwdParams& p, int id, int& b, int& h,
+                                                 int& qt) {
+  if (p.xcd_remap) {
+    const int xcd = id & 7, slot = id >> 3;
+    const int units = (p.B * p.Hkv) >> 3;  // (batch, kv-head) units per XCD
+    const int per_rank = units * p.G;
+    const int rank = slot / per_rank;
+    const int rem = slot - rank * per_rank;
+    const int ul = rem / p.G, gh = rem - ul * p.G;
+    const int u = ul * 8 + xcd;
+    b = u / p.Hkv;
+    const int kvh = u - b * p.Hkv;
+    h = kvh * p.G + gh;
+    qt = p.nqt - 1 - rank;
+  } else {
+    const int bh = p.B * p.H;
+    const int rank = id / bh;
+    const int rem = id - rank * bh;
+    b = rem / p.H;
+    h = rem - b * p.H;
+    qt = p.nqt - 1 - rank;
+  }
+}
+
+template <int D, bool COUNT>
+__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
+  using T = Tile<D>;
+  constexpr int BN = T::BN;
+  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, g = lane >> 5;
+
+  int b, h, qt;
+  decode_workgroup(p, blockIdx.x, b, h, qt);
+  const int kvh = h / p.G;
+  const int q0 = qt * kBM;
+  const int off = p.Nk - p.Nq;
+  const int q_last = min(q0 + kBM, p.Nq) - 1;
+  const long long p_lo = (long long)q0 + off, p_hi = (long long)q_last + off;
+
+  // Key range visible to any row of this work-group.
+  long long key_lo = 0, key_hi = p.Nk;  // [key_lo, key_hi)
+  if (p.causal) key_hi = min(key_hi, p_hi + 1);
+  else if (p.window > 0) key_hi = min(key_hi, p_hi + p.window + 1);
+  if (p.window > 0) key_lo = max(key_lo, p_lo - p.window);
+  const int kt_lo = key_hi > key_lo ? (int)(key_lo / BN) : 0;
+  const int kt_hi = key_hi > key_lo ? (int)((key_hi + BN - 1) / BN) : 0;
+  const int ntiles = kt_hi - kt_lo;
+
+  // This lane's query row and its Q fragments (B operand of S^T = K Q^T).
+  const int qrow = q0 + wave * 32 + l32;
+  const bool qvalid = qrow < p.Nq;
+  const long long qpos = (long long)qrow + off;
+  // Keys this row may see: [lo_q, hi_q] (used on boundary tiles only).
+  const long long lo_q = p.window > 0 ? qpos - p.window : 0;
+  long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)p.Nk - 1);
+  hi_q = min(hi_q, (long long)p.Nk - 1);
+  const size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+  bf16x8 qf[T::KS];
+  {
+    const uint16_t* qp = p.q + (head_q + (qvalid ? qrow : 0)) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qp + ks * 16, qvalid));
+  }
+
+  // Tile loader mapping: each thread moves one 4-key x 8-dim block of K and
+  // one of V per tile. K: dim-chunk fastest across lanes (coalesced rows).
+  // V: key-chunk fastest, so the transposed LDS writes of a wave land in
+  // consecutive slots of one V^T row.
+  const int kc_k = tid / T::DCH, dc_k = tid % T::DCH;
+  const int kc_v = tid % T::KCH, dc_v = tid / T::KCH;
+  const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
+  const uint16_t* kbase = p.k + head_kv * D;
+  const uint16_t* vbase = p.v + head_kv * D;
+  // V^T column of this thread's 4 keys: within each 16-key group the 4-key
+  // chunks are stored in the order 0, 2, 1, 3 so that lane half g finds its
+  // eight P-register keys {4g..4g+3, 8+4g..8+4g+3} contiguous.
+  const int vpos = (kc_v >> 2) * 16 + (((kc_v & 1) << 1) | ((kc_v >> 1) & 1)) * 4;
+
+  uint4 kreg[4], vreg[4];
+  int loaded = 0, masked = 0;
+
+  auto load_tile = [&](int kt) {
+    const int k0 = kt * BN;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int rk = k0 + kc_k * 4 + r;
+      kreg[r] = load16(kbase + (size_t)(rk < p.Nk ? rk : 0) * D + dc_k * 8, rk < p.Nk);
+      const int rv = k0 + kc_v * 4 + r;
+      vreg[r] = load16(vbase + (size_t)(rv < p.Nk ? rv : 0) * D + dc_v * 8, rv < p.Nk);
+    }
+    if (COUNT) ++loaded;
+  };
+
+  auto store_tile = [&](int buf) {
+    uint16_t* ks = smem + buf * T::STAGE;
+    uint16_t* vs = ks + BN * T::KSTR;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<uint4*>(ks + (kc_k * 4 + r) * T::KSTR + dc_k * 8) = kreg[r];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int w = e >> 1, half = e & 1;
+      uint2 col;
+      col.x = interleave16(u4_get(vreg[0], w), u4_get(vreg[1], w), half);
+      col.y = interleave16(u4_get(vreg[2], w), u4_get(vreg[3], w), half);
+      *reinterpret_cast<uint2*>(vs + (dc_v * 8 + e) * T::VSTR + vpos) = col;
+    }
+  };
+
+  // Does key tile kt need the per-element mask for any valid row here?
+  auto tile_partial = [&](int kt) -> bool {
+    const long long k0 = (long long)kt * BN, k1 = k0 + BN - 1;
+    if (k1 >= p.Nk) return true;
+    if (p.causal && k1 > p_lo) return true;
+    if (p.window > 0) {
+      if (k0 < p_hi - p.window) return true;
+      if (!p.causal && k1 > p_lo + p.window) return true;
+    }
+    return false;
+  };
+
+  f32x16 oacc[T::DB];
+#pragma unroll
+  for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
+  float m_ref = -kInf;  // reference row maximum, q.k units
+  // This lane's share of the row sum, twice: l_b sums the bf16-rounded P that
+  // multiply V (so the weights O is normalised by sum to one exactly), l_f the
+  // fp32 P (for an LSE as accurate as fp32 allows).
+  float l_b = 0.f, l_f = 0.f;
+
+  if (ntiles > 0) load_tile(kt_lo);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int kt = kt_lo + it;
+    const int buf = it & 1;
+    store_tile(buf);
+    __syncthreads();
+    if (it + 1 < ntiles) load_tile(kt + 1);
+
+    const uint16_t* ks = smem + buf * T::STAGE;
+    const uint16_t* vs = ks + BN * T::KSTR;
+
+    // S^T = K Q^T for this wave's 32 queries.
+    f32x16 sacc[T::KB];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb) {
+      sacc[kb] = f32x16{};
+      const uint16_t* kp = ks + (kb * 32 + l32) * T::KSTR + g * 8;
+#pragma unroll
+      for (int s = 0; s < T::KS; ++s) sacc[kb] = mfma32x32x16(lds_read_bf16x8(kp + s * 16), qf[s], sacc[kb]);
+    }
+    mfma_drain();
+
+    if (tile_partial(kt)) {
+      if (COUNT) ++masked;
+      // Key kt*BN + c + 4g is visible iff lo_q <= key <= hi_q; compare the
+      // compile-time offset c against the row's bounds relative to the tile.
+      const long long base = (long long)kt * BN + 4 * g;
+      const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
+      const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
+#pragma unroll
+      for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          sacc[kb][r] = ((c >= rl) & (c <= rh)) ? sacc[kb][r] : -kInf;
+        }
+    }
+
+    // Row maximum over this tile (16 keys per register block, two halves).
+    float mx = -kInf;
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = fmaxf(mx, swap_halves(mx));
+    const float m_new = fmaxf(m_ref, mx);
+    const bool need = m_new > m_ref + p.thr_raw;
+    if (wave_any(need)) {
+      const float alpha = need ? fast_exp2((m_ref - m_new) * p.scale_log2) : 1.f;
+      if (need) m_ref = m_new;
+      l_b *= alpha;
+      l_f *= alpha;
+#pragma unroll
+      for (int i = 0; i < T::DB; ++i) oacc[i] *= alpha;
+    }
+    const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
+
+    // P = exp2(s * scale * log2e - m), kept in registers as the B operand.
+    bf16x8 pf[T::PS];
+#pragma unroll
+    for (int kb = 0; kb < T::KB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x8 pv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pv[i] = fast_exp2(__builtin_fmaf(sacc[kb][hf * 8 + i], p.scale_log2, -msub));
+        l_f += sum_f32x8(pv);
+        pf[kb * 2 + hf] = to_bf16x8(pv);
+        l_b = sum_bf16x8(pf[kb * 2 + hf], l_b);
+      }
+
+    // O^T += V^T P^T.
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db) {
+      const uint16_t* vp = vs + (db * 32 + l32) * T::VSTR + g * 8;
+#pragma unroll
+      for (int t = 0; t < T::PS; ++t) oacc[db] = mfma32x32x16(lds_read_bf16x8(vp + t * 16), pf[t], oacc[db]);
+    }
+    mfma_drain();
+  }
+
+  // Epilogue: O = acc / l, LSE = m * scale + ln l.
+  const float lb = l_b + swap_halves(l_b);
+  const float lf = l_f + swap_halves(l_f);
+  const float inv = lb > 0.f ? 1.f / lb : 0.f;
+  if (qvalid) {
+    uint16_t* op = p.o + (head_q + qrow) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        uint2 w;
+        w.x = pack_bf16x2(oacc[db][rr * 4 + 0] * inv, oacc[db][rr * 4 + 1] * inv);
+        w.y = pack_bf16x2(oacc[db][rr * 4 + 2] * inv, oacc[db][rr * 4 + 3] * inv);
+        *reinterpret_cast<uint2*>(op + db * 32 + rr * 8) = w;
+      }
+    if (g == 0 && p.lse != nullptr)
+      p.lse[head_q + qrow] = lf > 0.f ? m_ref * p.scale + fast_log2(lf) * kLn2 : -kInf;
+  }
+  if (COUNT && tid == 0) {
+    int* c = p.counts + 2 * ((size_t)(b * p.H + h) * p.nqt + qt);
+    c[0] = loaded;
+    c[1] = masked;
+  }
+}
+
+template <int D>
+hipError_t launch_d(const FwdParams& prm, hipStream_t stream, bool count) {
+  const unsigned nblk = (unsigned)((size_t)prm.B * prm.H * prm.nqt);
+  void* args[] = {const_cast<FwdParams*>(&prm)};
+  const void* fn = count ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, true>)
+                         : reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false>);
+  return hipLaunchKernel(fn, dim3(nblk), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace
+
+void fwd_bf16_tile_shape(int d, int* block_m, int* block_n) {
+  *block_m = kBM;
+  *block_n = d == 128 ? Tile<128>::BN : Tile<64>::BN;
+}
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  FwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<uint16_t*>(a.o);
+  p.lse = a.lse;
+  p.B = a.B;
+  p.H = a.H;
+  p.Hkv = a.Hkv;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  p.G = a.H / a.Hkv;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  p.thr_raw = kRescaleThreshold / p.scale_log2;
+  p.causal = a.causal;
+  p.window = a.window;
+  p.nqt = (a.Nq + kBM - 1) / kBM;
+  p.xcd_remap = ((a.B * a.Hkv) % 8 == 0) ? 1 : 0;
+  p.counts = a.counts;
+  if (log_enabled())
+    fprintf(stderr, "[miattn] fwd_bf16 d=%d grid=%lld block=%d BM=%d BN=%d xcd_remap=%d\n", a.d,
+            (long long)a.B * a.H * p.nqt, kThreads, kBM, a.d == 128 ? 64 : 128, p.xcd_remap);
+  const bool count = a.counts != nullptr;
+  return a.d == 128 ? launch_d<128>(p, stream, count) : launch_d<64>(p, stream, count);
+}
+
+}  // namespace miattn

@@ -1,0 +1,48 @@
+// Host-side launchers of the libmiattn kernels. Arguments reaching these
+// functions have already been validated by the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+
+namespace miattn {
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal, window;
+  int* counts;  // optional per-work-group (tiles loaded, tiles masked)
+};
+
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int B, H, Hkv, Nk, d;
+  float scale;
+  int window;
+  int splits;
+  void* workspace;
+};
+
+// Query-tile rows / key-tile columns of the bf16 and fp32 forward kernels.
+void fwd_bf16_tile_shape(int d, int* block_m, int* block_n);
+void fwd_f32_tile_shape(int d, int* block_m, int* block_n);
+
+hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+// Partials layout inside the workspace: O_s fp32 [B, H, S, d], then lse_s fp32 [B, H, S].
+size_t decode_workspace_bytes(int B, int H, int d, int splits);
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+bool log_enabled();
+
+}  // namespace miattn

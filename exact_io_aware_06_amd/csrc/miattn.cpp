@@ -1,0 +1,181 @@
+// libmiattn C ABI: argument validation, kernel selection, launch.
+//
+// Every argument is checked before the first HIP call so that argument errors
+// are reported without touching (or needing) a device. No device memory is
+// allocated here and nothing is synchronised.
+
+#include <hip/hip_runtime_api.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+
+#include "launch.hpp"
+#include "miattn.h"
+
+namespace miattn {
+
+bool log_enabled() {
+  static const bool on = [] {
+    const char* e = std::getenv("MIATTN_LOG");
+    return e != nullptr && e[0] != '\0' && e[0] != '0';
+  }();
+  return on;
+}
+
+}  // namespace miattn
+
+namespace {
+
+using miattn::DecodeArgs;
+using miattn::FwdArgs;
+
+int device_status() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) {
+    (void)hipGetLastError();  // do not leave a sticky error for the caller
+    return MIATTN_ENODEVICE;
+  }
+  return MIATTN_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MIATTN_OK : MIATTN_ELAUNCH; }
+
+bool valid_scale(float s) { return std::isfinite(s) && s > 0.f; }
+
+// Shared checks of the two forward entry points.
+int check_fwd(const void* q, const void* k, const void* v, const void* o, int B, int H, int Hkv,
+              int Nq, int Nk, int d, float scale, int causal, int window, int block_m) {
+  if (B < 0 || H < 1 || Hkv < 1 || Nq < 0 || Nk < 0) return MIATTN_EINVAL;
+  if (H % Hkv != 0) return MIATTN_EINVAL;
+  if (causal != 0 && causal != 1) return MIATTN_EINVAL;
+  if (window < 0) return MIATTN_EINVAL;
+  if (!valid_scale(scale)) return MIATTN_EINVAL;
+  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
+  const long long nq_elems = (long long)B * H * Nq;
+  const long long nk_elems = (long long)B * Hkv * Nk;
+  if (nq_elems > 0 && (q == nullptr || o == nullptr)) return MIATTN_EINVAL;
+  if (nq_elems > 0 && nk_elems > 0 && (k == nullptr || v == nullptr)) return MIATTN_EINVAL;
+  // one work-group per (batch, head, query tile) in a 1-D grid
+  const long long nqt = ((long long)Nq + block_m - 1) / block_m;
+  if ((long long)B * H * nqt > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  return MIATTN_OK;
+}
+
+int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, float* lse, int B,
+            int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+            int* counts, void* stream) {
+  int bm = 0, bn = 0;
+  if (d == 64 || d == 128) {
+    if (f32) miattn::fwd_f32_tile_shape(d, &bm, &bn);
+    else miattn::fwd_bf16_tile_shape(d, &bm, &bn);
+  } else {
+    bm = 1;
+  }
+  int st = check_fwd(q, k, v, o, B, H, Hkv, Nq, Nk, d, scale, causal, window, bm);
+  if (st != MIATTN_OK) return st;
+  if (B == 0 || Nq == 0) return MIATTN_OK;  // nothing to compute
+  if ((st = device_status()) != MIATTN_OK) return st;
+  FwdArgs a{q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, counts};
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return launch_status(f32 ? miattn::launch_fwd_f32(a, s) : miattn::launch_fwd_bf16(a, s));
+}
+
+int resolve_splits(int B, int Hkv, int Nk, int num_splits) {
+  if (B < 0 || Hkv < 1 || Nk < 0 || num_splits < 0) return MIATTN_EINVAL;
+  if (num_splits > 0) {
+    if (Nk > 0 && num_splits > Nk) return MIATTN_EINVAL;
+    if (Nk == 0 && num_splits > 1) return MIATTN_EINVAL;
+    return num_splits;
+  }
+  // Library choice: enough work-groups to fill the chip several times over
+  // (about 2048), with chunks of at least 512 keys.
+  const long long units = (long long)B * Hkv;
+  if (units == 0 || Nk == 0) return 1;
+  long long want = (2048 + units - 1) / units;
+  const long long cap = (Nk + 511) / 512;
+  if (want > cap) want = cap;
+  if (want < 1) want = 1;
+  return (int)want;
+}
+
+}  // namespace
+
+extern "C" {
+
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+             int Hkv, int Nq, int Nk, int d, float scale, int causal, int window, void* stream) {
+  return run_fwd(false, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, nullptr,
+                 stream);
+}
+
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse, int B,
+                 int H, int Hkv, int Nq, int Nk, int d, float scale, int causal, int window,
+                 void* stream) {
+  return run_fwd(true, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, nullptr,
+                 stream);
+}
+
+int attn_fwd_tile_counts(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                         int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
+                         int window, int* counts, void* stream) {
+  if (counts == nullptr && (long long)B * H * Nq > 0) return MIATTN_EINVAL;
+  return run_fwd(false, q, k, v, o, lse, B, H, Hkv, Nq, Nk, d, scale, causal, window, counts,
+                 stream);
+}
+
+int attn_fwd_tile_shape(int d, int is_f32, int* block_m, int* block_n) {
+  if (block_m == nullptr || block_n == nullptr) return MIATTN_EINVAL;
+  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
+  if (is_f32) miattn::fwd_f32_tile_shape(d, block_m, block_n);
+  else miattn::fwd_bf16_tile_shape(d, block_m, block_n);
+  return MIATTN_OK;
+}
+
+int attn_decode_num_splits(int B, int Hkv, int Nk, int num_splits) {
+  return resolve_splits(B, Hkv, Nk, num_splits);
+}
+
+size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits) {
+  const int S = resolve_splits(B, Hkv, Nk, num_splits);
+  if (S < 0 || B < 0 || H < 1 || d < 1) return 0;
+  return miattn::decode_workspace_bytes(B, H, d, S);
+}
+
+int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, void* o,
+                       float* lse, int B, int H, int Hkv, int Nk, int d, float scale, int window,
+                       int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || H < 1 || Hkv < 1 || Nk < 0) return MIATTN_EINVAL;
+  if (H % Hkv != 0) return MIATTN_EINVAL;
+  if (window < 0 || !valid_scale(scale)) return MIATTN_EINVAL;
+  const int S = resolve_splits(B, Hkv, Nk, num_splits);
+  if (S < 0) return S;
+  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
+  if (H / Hkv > 32) return MIATTN_EUNSUPPORTED;
+  if ((long long)B * Hkv * S > (long long)INT_MAX || (long long)B * H > (long long)INT_MAX)
+    return MIATTN_EUNSUPPORTED;
+  if (B == 0) return MIATTN_OK;
+  if (q == nullptr || o == nullptr) return MIATTN_EINVAL;
+  if (Nk > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
+  const size_t need = miattn::decode_workspace_bytes(B, H, d, S);
+  if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
+  int st = device_status();
+  if (st != MIATTN_OK) return st;
+  DecodeArgs a{q, k_cache, v_cache, o, lse, B, H, Hkv, Nk, d, scale, window, S, workspace};
+  return launch_status(miattn::launch_decode(a, static_cast<hipStream_t>(stream)));
+}
+
+const char* attn_strerror(int status) {
+  switch (status) {
+    case MIATTN_OK: return "success";
+    case MIATTN_EINVAL: return "invalid argument";
+    case MIATTN_EUNSUPPORTED: return "unsupported configuration";
+    case MIATTN_ELAUNCH: return "kernel launch failed";
+    case MIATTN_EWORKSPACE: return "decode workspace missing or too small";
+    case MIATTN_ENODEVICE: return "no HIP device available";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

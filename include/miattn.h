@@ -1,0 +1,143 @@
+/*
+ * libmiattn - exact fused scaled-dot-product attention on AMD Instinct MI355X
+ * (gfx950), behind a plain C ABI.
+ *
+ * What is computed (every entry point): for batch b, query head h, query row
+ * i and key j,
+ *
+ *     s_ij   = scale * sum_c q[b,h,i,c] * k[b,kvh,j,c]     (visible pairs only)
+ *     O[b,h,i,:] = sum_j softmax_j(s_i.) * v[b,kvh,j,:]
+ *     LSE[b,h,i] = ln sum_j exp(s_ij)
+ *
+ * i.e. softmax(Q K^T / sqrt(d)) V as defined in "Chapter 3.1 - The Cost of
+ * Attention" (section 2, "Why self-attention is quadratic, precisely"), with
+ * `scale` standing in for 1/sqrt(d). The forward pass is one fused, tiled
+ * kernel with an online softmax: the score matrix never reaches device memory
+ * ("Quadratic Complexity Bottleneck", FlashAttention entry; grasp.study
+ * efficient-attention lesson, "Tiling and Kernel Fusion" and "Online
+ * Softmax"). The result equals the one-shot softmax up to rounding.
+ *
+ * Conventions shared by all entry points
+ *   Layout    contiguous row-major. q, o: [B, H, Nq, d]; k, v: [B, Hkv, Nk, d];
+ *             lse: [B, H, Nq]. Decode: q, o: [B, H, d]; caches [B, Hkv, Nk, d];
+ *             lse [B, H].
+ *   bf16      "bf16" tensors hold bfloat16 bit patterns (uint16). Outputs are
+ *             rounded once, to nearest even, from fp32. Accumulation is fp32.
+ *   GQA       query heads form Hkv contiguous groups of G = H / Hkv heads; head
+ *             h reads K/V head h / G ("Quadratic Complexity Bottleneck", GQA
+ *             and MQA entries). H % Hkv != 0 is MIATTN_EINVAL.
+ *   causal    0 or 1. Query row i sits at absolute position p = i + Nk - Nq
+ *             (bottom-right alignment), so a single query row sees the whole
+ *             cache.
+ *   window    0 = no window. W > 0: a query at position p sees keys
+ *             j in [p - W, p] when causal (W keys to its left plus itself),
+ *             |p - j| <= W otherwise ("Quadratic Complexity Bottleneck",
+ *             sliding-window entry). Negative is MIATTN_EINVAL.
+ *   scale     used exactly as passed; must be finite and > 0.
+ *   empty     a query row that sees no key gets O = 0 and LSE = -inf. B, Nq
+ *             or Nk may be 0 (Nk = 0 makes every row empty; B = 0 or Nq = 0
+ *             does nothing). Pointers to tensors with no elements may be NULL.
+ *   d         64 or 128, else MIATTN_EUNSUPPORTED.
+ *   lse       may be NULL: the LSE store is skipped.
+ *   stream    a hipStream_t (NULL = the null stream). Work is enqueued
+ *             asynchronously; no entry point synchronises.
+ *
+ * Ownership: the caller owns every buffer, including the decode workspace,
+ * and keeps it alive until the stream work completes. The library allocates
+ * and frees no device memory, keeps no pointer after returning, and holds no
+ * per-call state. Calls are thread-safe.
+ *
+ * Errors: the return value is a status. Arguments are validated before any
+ * HIP call, so argument errors return without touching the device. A failed
+ * launch returns MIATTN_ELAUNCH. Faults inside a kernel surface at the
+ * caller's next synchronisation, as with any asynchronous launch.
+ */
+#ifndef MIATTN_H
+#define MIATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MIATTN_OK            0
+#define MIATTN_EINVAL       -1 /* bad argument: null pointer, negative size, H % Hkv, ... */
+#define MIATTN_EUNSUPPORTED -2 /* valid but not built: d not 64/128, decode G > 32 */
+#define MIATTN_ELAUNCH      -3 /* the HIP runtime refused a launch */
+#define MIATTN_EWORKSPACE   -4 /* decode workspace NULL or smaller than required */
+#define MIATTN_ENODEVICE    -5 /* no HIP device is visible to this process */
+
+/*
+ * Prefill / training forward, bfloat16 in and out, fp32 LSE.
+ * Steps: Q tile loaded once; K/V tiles streamed through LDS (skipping every
+ * tile the causal / window mask hides entirely); S = Q K^T on bf16 matrix
+ * cores with fp32 accumulation; the mask applied on boundary tiles only;
+ * online-softmax update of the running row max and sum; O += P V; one
+ * normalise-and-store at the end ("Chapter 3.1 - The Cost of Attention",
+ * section 5; "Attention Research", section 2 for the sequence-parallel
+ * partitioning of the query rows).
+ */
+int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+             int B, int H, int Hkv, int Nq, int Nk, int d,
+             float scale, int causal, int window, void* stream);
+
+/* Same contract with fp32 q, k, v, o; the whole computation is fp32, with no
+ * bf16 rounding anywhere. */
+int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
+                 int B, int H, int Hkv, int Nq, int Nk, int d,
+                 float scale, int causal, int window, void* stream);
+
+/*
+ * Split-K decode: one query token per sequence against a KV cache
+ * ("Quadratic Complexity Bottleneck", KV cache entry: past K and V are read
+ * from the cache; "Attention Research", section 2: split-K over keys for
+ * decode). The new token's K/V are already in the cache, so the query sits at
+ * position Nk - 1 and sees every key (or the last window + 1 keys).
+ *
+ * The key range is cut into `num_splits` contiguous chunks of C = ceil(Nk/S)
+ * keys (the last shorter, trailing ones possibly empty). A first kernel turns
+ * each (sequence, KV head, chunk) into a normalised partial output O_s and its
+ * log-sum-exp lse_s for all G query heads of the group, reading each K/V byte
+ * once; a second kernel merges the partials: LSE = ln sum_s exp(lse_s),
+ * O = sum_s exp(lse_s - LSE) O_s, a chunk with no visible key weighing 0.
+ *
+ * q, o: [B, H, d] bf16; k_cache, v_cache: [B, Hkv, Nk, d] bf16; lse [B, H]
+ * fp32 or NULL. num_splits: 1..Nk, or 0 to let the library choose.
+ * workspace: device memory of at least attn_decode_workspace_bytes(...) with
+ * the same arguments (else MIATTN_EWORKSPACE). G = H / Hkv must be <= 32.
+ */
+size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits);
+int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
+                       void* o, float* lse,
+                       int B, int H, int Hkv, int Nk, int d, float scale, int window,
+                       int num_splits, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* The split count attn_decode_splitk uses for these arguments (resolves 0),
+ * or a negative status for invalid ones. */
+int attn_decode_num_splits(int B, int Hkv, int Nk, int num_splits);
+
+/* Query-tile (block_m) and key-tile (block_n) sizes of the forward kernels
+ * for head dim d; is_f32 selects the fp32 kernel. Returns a status. */
+int attn_fwd_tile_shape(int d, int is_f32, int* block_m, int* block_n);
+
+/*
+ * Instrumented attn_fwd (bf16): runs the same kernel and also writes, per
+ * work-group, how many K/V tiles it loaded and how many of those it masked.
+ * counts: device int32 [B, H, ceil(Nq / block_m), 2]. Used to show that tiles
+ * the mask hides entirely are never loaded ("Attention Research", section 4:
+ * a FLOP reduction only pays if the kernel skips whole blocks).
+ */
+int attn_fwd_tile_counts(const void* q, const void* k, const void* v, void* o, float* lse,
+                         int B, int H, int Hkv, int Nq, int Nk, int d,
+                         float scale, int causal, int window, int* counts, void* stream);
+
+/* Static string for a status code. */
+const char* attn_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MIATTN_H */
