@@ -56,22 +56,20 @@ def traffic_for(kind: str):
     return t.get("bytes_per_launch")
 
 
-def cpu_baseline_prefill(cfg, heads: int):
-    """The oracle, untuned, on `heads` heads of the prefill workload."""
-    import numpy as np
-    import torch
+def cpu_baseline_prefill(cfg, heads: int, q, k, v):
+    """The oracle, untuned, on the first `heads` heads of the prefill workload.
+
+    q, k, v are host copies of the benchmarked tensors (first `heads` query
+    heads and their K/V heads).
+    """
     from threadpoolctl import threadpool_info
 
     import oracle
-    import synth
     from exact_io_aware_06_amd import accounting
 
     sub = cfg.with_(H=heads, Hkv=max(1, heads * cfg.Hkv // cfg.H))
-    q, k, v = synth.prefill_inputs(sub, seed=0)
-    q64 = q.double().numpy()
-    k64, v64 = k.double().numpy(), v.double().numpy()
     t0 = time.perf_counter()
-    oracle.attention_ref(q64, k64, v64, sub.scale, sub.causal, sub.window)
+    oracle.attention_ref(q, k, v, sub.scale, sub.causal, sub.window)
     dt = time.perf_counter() - t0
     flops = accounting.prefill_flops(1, heads, sub.Nq, sub.Nk, sub.d, sub.causal, sub.window)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -81,16 +79,14 @@ def cpu_baseline_prefill(cfg, heads: int):
             "seconds": dt}
 
 
-def cpu_baseline_decode(cfg, seqs: int):
-    import torch
+def cpu_baseline_decode(cfg, seqs: int, q, kc, vc):
+    """The oracle, untuned, on host copies of the first `seqs` decode sequences."""
     from threadpoolctl import threadpool_info
 
     import oracle
-    import synth
     from exact_io_aware_06_amd import accounting
 
     sub = cfg.with_(B=seqs)
-    q, kc, vc = synth.decode_inputs(sub, seed=0)
     t0 = time.perf_counter()
     oracle.decode_ref(q, kc, vc, sub.scale, sub.window)
     dt = time.perf_counter() - t0
@@ -107,8 +103,12 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-heads", type=int, default=4)
-    ap.add_argument("--cpu-seqs", type=int, default=2)
+    ap.add_argument("--cpu-heads", type=int, default=32)
+    ap.add_argument("--cpu-seqs", type=int, default=16)
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32"], default="all",
+                    help="launch only one part of the step (for profiling runs)")
+    ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
+                    help="also run one plain device copy of MIB MiB (counter calibration)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -145,20 +145,38 @@ def main():
     of = torch.empty_like(qf)
     lsef = torch.empty(cf.B, cf.H, cf.Nq, dtype=torch.float32, device=dev)
 
+    run_pre = args.only in ("all", "prefill")
+    run_dec = args.only in ("all", "decode")
+    run_f32 = args.only in ("all", "fp32")
+
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal, window=cp.window, out=o, lse=lse)
+        if run_pre:
+            mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal, window=cp.window, out=o,
+                        lse=lse)
         if ev is not None:
             ev[1].record()
-        mi.attn_decode(qd, kc, vc, scale=cd.scale, window=cd.window, num_splits=cd.splits,
-                       out=od, lse=lsed, workspace=ws)
+        if run_dec:
+            mi.attn_decode(qd, kc, vc, scale=cd.scale, window=cd.window, num_splits=cd.splits,
+                           out=od, lse=lsed, workspace=ws)
         if ev is not None:
             ev[2].record()
-        mi.attn_fwd(qf, kf, vf, scale=cf.scale, causal=cf.causal, window=cf.window, out=of,
-                    lse=lsef)
+        if run_f32:
+            mi.attn_fwd(qf, kf, vf, scale=cf.scale, causal=cf.causal, window=cf.window, out=of,
+                        lse=lsef)
         if ev is not None:
             ev[3].record()
+
+    if args.calib_copy > 0:
+        nbytes = args.calib_copy << 20
+        src = torch.empty(nbytes // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written", file=sys.stderr)
+        del src, dst
 
     for _ in range(args.warmup):
         step()
@@ -178,8 +196,16 @@ def main():
     pre_flops = accounting.prefill_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
     dec_bytes = accounting.decode_bytes(cd.B, cd.H, cd.Hkv, cd.Nk, cd.d, window=cd.window)
     f32_flops = accounting.prefill_flops(cf.B, cf.H, cf.Nq, cf.Nk, cf.d, cf.causal, cf.window)
-    pre_tflops = pre_flops / (mean(pre_ms) * 1e-3) / 1e12
-    dec_gbs = dec_bytes / (mean(dec_ms) * 1e-3) / 1e9
+    rate = lambda work, ms: work / (ms * 1e-3) if ms > 0 else 0.0
+    pre_tflops = rate(pre_flops, mean(pre_ms)) / 1e12
+    dec_gbs = rate(dec_bytes, mean(dec_ms)) / 1e9
+    if args.only != "all":
+        part = {"prefill": (pre_ms, pre_tflops, "TFLOP/s"), "decode": (dec_ms, dec_gbs, "GB/s"),
+                "fp32": (f32_ms, rate(f32_flops, mean(f32_ms)) / 1e12, "TFLOP/s")}[args.only]
+        print(json.dumps({"only": args.only, "ms": round(mean(part[0]), 4),
+                          "ms_min": round(min(part[0]), 4), "value": round(part[1], 2),
+                          "unit": part[2], "steps": args.steps}))
+        return
 
     out = {
         "metric": METRIC,
@@ -209,7 +235,7 @@ def main():
         "decode": {"value": round(dec_gbs, 1), "unit": "GB/s", "ms": round(mean(dec_ms), 4),
                    "ms_min": round(min(dec_ms), 4), "frac_hbm": round(dec_gbs / PEAK_HBM_GBS, 4)},
         "fp32_forward": {"ms": round(mean(f32_ms), 4),
-                         "tflops": round(f32_flops / (mean(f32_ms) * 1e-3) / 1e12, 3)},
+                         "tflops": round(rate(f32_flops, mean(f32_ms)) / 1e12, 3)},
         "roofline": {"kernel": "fwd_bf16_kernel<128>", "bound": "mfma",
                      "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
@@ -220,13 +246,19 @@ def main():
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_for("decode")},
     }
+    if not args.no_cpu_baseline:
+        nh = max(1, min(args.cpu_heads, cp.H))
+        nkv = max(1, nh * cp.Hkv // cp.H)
+        host = [t.cpu() for t in (q[:, :nh], k[:, :nkv], v[:, :nkv])]
+        ns = max(1, min(args.cpu_seqs, cd.B))
+        host_d = [t.cpu() for t in (qd[:ns], kc[:ns], vc[:ns])]
     del kc, vc
     torch.cuda.empty_cache()
     if not args.no_cpu_baseline:
-        cb = cpu_baseline_prefill(cp, args.cpu_heads)
+        cb = cpu_baseline_prefill(cp, nh, *host)
         out["cpu_baseline"] = {kk: (round(vv, 6) if isinstance(vv, float) else vv)
                                for kk, vv in cb.items() if kk != "seconds"}
-        cbd = cpu_baseline_decode(cd, args.cpu_seqs)
+        cbd = cpu_baseline_decode(cd, ns, *host_d)
         out["cpu_baseline_decode"] = {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                                       for kk, vv in cbd.items() if kk != "seconds"}
     print(json.dumps(out))
