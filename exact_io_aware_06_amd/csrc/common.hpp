@@ -15,6 +15,44 @@ constexpr float kInf = __builtin_huge_valf();
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
+// ---- LDS, buffer and DMA helpers -------------------------------------------
+
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ lds_u8* lds_ptr(void* shared_array) {
+  return (lds_u8*)(shared_array);
+}
+
+// 16-byte LDS read at a byte offset.
+__device__ __forceinline__ bf16x8 lds_b128(const lds_u8* base, uint32_t off) {
+  return __builtin_bit_cast(bf16x8, *(const __attribute__((address_space(3))) uint4*)(base + off));
+}
+
+// Transposing LDS read of 16-bit elements. Within each group of 16 lanes,
+// lane j names an 8-byte chunk (4 elements); lane i = 4a + c receives element
+// c of the chunks named by lanes a, a + 4, a + 8 and a + 12, in that order.
+__device__ __forceinline__ uint2 lds_tr_b64(const lds_u8* base, uint32_t off) {
+  const i16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(base + off));
+  return __builtin_bit_cast(uint2, r);
+}
+
+// Raw buffer resource over [base, base + bytes): loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+
+// Global -> LDS copy of 16 bytes per lane: lane L's bytes at `voff` land at
+// dst + 16 L. `dst` must be wave-uniform.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* dst, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, 0, 0, 0);
+}
+
+// s_waitcnt vmcnt(0): every vector-memory load of this wave (DMA included) done.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // 16-byte global load that yields zeros when `ok` is false.
 __device__ __forceinline__ uint4 load16(const uint16_t* p, bool ok) {
   uint4 r = make_uint4(0u, 0u, 0u, 0u);

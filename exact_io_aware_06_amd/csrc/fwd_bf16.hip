@@ -68,17 +68,29 @@ struct FwdParams {
 template <int D>
 struct Tile {
   static constexpr int BN = (D == 128) ? 64 : 128;  // keys per K/V tile
-  static constexpr int KSTR = D + 8;                 // K row stride in LDS (elements)
-  static constexpr int VSTR = BN + 8;                // V^T row stride in LDS (elements)
-  static constexpr int STAGE = BN * KSTR + D * VSTR; // elements per LDS stage
+  static constexpr int ROWB = D * 2;                 // bytes per K/V row
+  static constexpr int CPR = D / 8;                  // 16-byte chunks per row
+  static constexpr int RPB = 64 / CPR;               // rows per 1 KB DMA block
+  static constexpr int TILE = BN * ROWB;             // bytes of one K (or V) tile
+  static constexpr int NBLK = TILE / 1024;           // DMA blocks per tile and tensor
+  static constexpr int BPW = NBLK / 4;               // ... per wave
+  static constexpr int STAGE = 2 * TILE;             // one pipeline stage: K tile, V tile
   static constexpr int KB = BN / 32;                 // 32-key blocks per tile
   static constexpr int DB = D / 32;                  // 32-dim blocks of O
   static constexpr int KS = D / 16;                  // k-steps of Q K^T
   static constexpr int PS = BN / 16;                 // k-steps of P V
-  static constexpr int DCH = D / 8;                  // 8-element chunks per row
-  static constexpr int KCH = BN / 4;                 // 4-key chunks per tile
-  static_assert(KCH * DCH == kThreads, "one 4x8 block per thread per tile");
+  static_assert(NBLK % 4 == 0, "DMA blocks split over four waves");
 };
+
+// LDS layout of a K or V tile: row-major [key][d] with the 16-byte chunks of
+// each row permuted by an XOR swizzle, so that 16 lanes reading one chunk of
+// 16 consecutive rows (Q K^T operand) and 16 lanes reading 4 rows x 32 bytes
+// (transposing V^T reads) both hit distinct banks.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  return (r >> 1) & 7;
+}
 
 __device__ __forceinline__ void decode_workgroup(const FwdParams& p, int id, int& b, int& h,
                                                  int& qt) {
@@ -108,10 +120,12 @@ template <int D, bool COUNT>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   using T = Tile<D>;
   constexpr int BN = T::BN;
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::STAGE];
+  lds_u8* const L = lds_ptr(smem);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
 
   int b, h, qt;
@@ -147,49 +161,62 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qp + ks * 16, qvalid));
   }
 
-  // Tile loader mapping: each thread moves one 4-key x 8-dim block of K and
-  // one of V per tile. K: dim-chunk fastest across lanes (coalesced rows).
-  // V: key-chunk fastest, so the transposed LDS writes of a wave land in
-  // consecutive slots of one V^T row.
-  const int kc_k = tid / T::DCH, dc_k = tid % T::DCH;
-  const int kc_v = tid % T::KCH, dc_v = tid / T::KCH;
+  // Per-lane LDS byte offsets, fixed for the whole kernel.
+  // Q K^T operand: row kb*32 + l32, chunk 2 ks + g.
+  uint32_t koff[T::KS];
+  {
+    const int sw = swz<D>(l32);
+#pragma unroll
+    for (int ks = 0; ks < T::KS; ++ks)
+      koff[ks] = (uint32_t)(l32 * T::ROWB + (((2 * ks + g) ^ sw) << 4));
+  }
+  // V^T operand via transposing reads: as a source lane of its 16-lane group,
+  // this lane names rows 4g + e (+8 for the second read) and dims
+  // db*32 + 16h + 4a' of each 16-key step; lane 16h + i then receives dims
+  // 16h + i of keys 4g..4g+3 (first read) and 8+4g..8+4g+3 (second read),
+  // exactly the keys its P registers hold.
+  uint32_t voff[T::DB][2];
+  {
+    const int j = lane & 15, a = j & 3, e = j >> 2, hh = (lane >> 4) & 1;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int r = 4 * g + e + 8 * qh;
+      const int sw = swz<D>(r);
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int c = 4 * db + 2 * hh + (a >> 1);
+        voff[db][qh] = (uint32_t)(T::TILE + r * T::ROWB + ((c ^ sw) << 4) + (a & 1) * 8);
+      }
+    }
+  }
+  // DMA: block blk of a tile holds rows blk*RPB .. +RPB; lane L moves chunk
+  // (L % CPR) ^ swz(row) of row blk*RPB + L / CPR into LDS slot L.
+  uint32_t dvoff[T::BPW];
+#pragma unroll
+  for (int i = 0; i < T::BPW; ++i) {
+    const int blk = wave * T::BPW + i;
+    const int r = blk * T::RPB + lane / T::CPR;
+    dvoff[i] = (uint32_t)(r * T::ROWB + (((lane % T::CPR) ^ swz<D>(r)) << 4));
+  }
+
   const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
   const uint16_t* kbase = p.k + head_kv * D;
   const uint16_t* vbase = p.v + head_kv * D;
-  // V^T column of this thread's 4 keys: within each 16-key group the 4-key
-  // chunks are stored in the order 0, 2, 1, 3 so that lane half g finds its
-  // eight P-register keys {4g..4g+3, 8+4g..8+4g+3} contiguous.
-  const int vpos = (kc_v >> 2) * 16 + (((kc_v & 1) << 1) | ((kc_v >> 1) & 1)) * 4;
-
-  uint4 kreg[4], vreg[4];
   int loaded = 0, masked = 0;
 
-  auto load_tile = [&](int kt) {
-    const int k0 = kt * BN;
+  // Issue the K and V DMA of key tile kt into pipeline stage stg.
+  auto issue = [&](int kt, int stg) {
+    const long long k0 = (long long)kt * BN;
+    const uint32_t bytes = k0 < p.Nk ? (uint32_t)((p.Nk - k0) * T::ROWB) : 0u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + k0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + k0 * D, bytes);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int rk = k0 + kc_k * 4 + r;
-      kreg[r] = load16(kbase + (size_t)(rk < p.Nk ? rk : 0) * D + dc_k * 8, rk < p.Nk);
-      const int rv = k0 + kc_v * 4 + r;
-      vreg[r] = load16(vbase + (size_t)(rv < p.Nk ? rv : 0) * D + dc_v * 8, rv < p.Nk);
+    for (int i = 0; i < T::BPW; ++i) {
+      lds_u8* dst = L + stg * T::STAGE + (wave * T::BPW + i) * 1024;
+      dma16(rk, dst, dvoff[i]);
+      dma16(rv, dst + T::TILE, dvoff[i]);
     }
     if (COUNT) ++loaded;
-  };
-
-  auto store_tile = [&](int buf) {
-    uint16_t* ks = smem + buf * T::STAGE;
-    uint16_t* vs = ks + BN * T::KSTR;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-      *reinterpret_cast<uint4*>(ks + (kc_k * 4 + r) * T::KSTR + dc_k * 8) = kreg[r];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int w = e >> 1, half = e & 1;
-      uint2 col;
-      col.x = interleave16(u4_get(vreg[0], w), u4_get(vreg[1], w), half);
-      col.y = interleave16(u4_get(vreg[2], w), u4_get(vreg[3], w), half);
-      *reinterpret_cast<uint2*>(vs + (dc_v * 8 + e) * T::VSTR + vpos) = col;
-    }
   };
 
   // Does key tile kt need the per-element mask for any valid row here?
@@ -213,26 +240,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // fp32 P (for an LSE as accurate as fp32 allows).
   float l_b = 0.f, l_f = 0.f;
 
-  if (ntiles > 0) load_tile(kt_lo);
-
-  for (int it = 0; it < ntiles; ++it) {
-    const int kt = kt_lo + it;
-    const int buf = it & 1;
-    store_tile(buf);
-    __syncthreads();
-    if (it + 1 < ntiles) load_tile(kt + 1);
-
-    const uint16_t* ks = smem + buf * T::STAGE;
-    const uint16_t* vs = ks + BN * T::KSTR;
-
+  auto compute = [&](int kt, int stg) {
+    const lds_u8* st = L + stg * T::STAGE;
     // S^T = K Q^T for this wave's 32 queries.
     f32x16 sacc[T::KB];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
       sacc[kb] = f32x16{};
-      const uint16_t* kp = ks + (kb * 32 + l32) * T::KSTR + g * 8;
 #pragma unroll
-      for (int s = 0; s < T::KS; ++s) sacc[kb] = mfma32x32x16(lds_read_bf16x8(kp + s * 16), qf[s], sacc[kb]);
+      for (int ks = 0; ks < T::KS; ++ks)
+        sacc[kb] = mfma32x32x16(lds_b128(st, koff[ks] + kb * 32 * T::ROWB), qf[ks], sacc[kb]);
     }
     mfma_drain();
 
@@ -288,13 +305,38 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
     // O^T += V^T P^T.
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-      const uint16_t* vp = vs + (db * 32 + l32) * T::VSTR + g * 8;
+    for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-      for (int t = 0; t < T::PS; ++t) oacc[db] = mfma32x32x16(lds_read_bf16x8(vp + t * 16), pf[t], oacc[db]);
-    }
-    mfma_drain();
+      for (int t = 0; t < T::PS; ++t) {
+        const uint2 lo = lds_tr_b64(st, voff[db][0] + t * 16 * T::ROWB);
+        const uint2 hi = lds_tr_b64(st, voff[db][1] + t * 16 * T::ROWB);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        oacc[db] = mfma32x32x16(va, pf[t], oacc[db]);
+      }
+  };
+
+  // Two-stage pipeline: while tile i is computed from one stage, the DMA of
+  // tile i + 1 fills the other; one barrier per tile both publishes the new
+  // stage and retires the old one. Unrolled by two so stage offsets fold into
+  // instruction immediates.
+  if (ntiles > 0) {
+    issue(kt_lo, 0);
+    wait_vmem();
+    __syncthreads();
   }
+  for (int it = 0; it < ntiles; it += 2) {
+    if (it + 1 < ntiles) issue(kt_lo + it + 1, 1);
+    compute(kt_lo + it, 0);
+    wait_vmem();
+    __syncthreads();
+    if (it + 1 < ntiles) {
+      if (it + 2 < ntiles) issue(kt_lo + it + 2, 0);
+      compute(kt_lo + it + 1, 1);
+      wait_vmem();
+      __syncthreads();
+    }
+  }
+  mfma_drain();
 
   // Epilogue: O = acc / l, LSE = m * scale + ln l.
   const float lb = l_b + swap_halves(l_b);

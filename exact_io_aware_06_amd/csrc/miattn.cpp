@@ -60,6 +60,8 @@ int check_fwd(const void* q, const void* k, const void* v, const void* o, int B,
   // one work-group per (batch, head, query tile) in a 1-D grid
   const long long nqt = ((long long)Nq + block_m - 1) / block_m;
   if ((long long)B * H * nqt > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  // K/V of one head are addressed through 32-bit buffer offsets
+  if ((long long)Nk * d * 4 > 0xFFFFFFFFLL) return MIATTN_EUNSUPPORTED;
   return MIATTN_OK;
 }
 

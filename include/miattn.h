@@ -38,6 +38,8 @@
  *             or Nk may be 0 (Nk = 0 makes every row empty; B = 0 or Nq = 0
  *             does nothing). Pointers to tensors with no elements may be NULL.
  *   d         64 or 128, else MIATTN_EUNSUPPORTED.
+ *   sizes     one head's K (or V) must stay under 4 GiB in fp32 terms
+ *             (Nk * d * 4 < 2^32), else MIATTN_EUNSUPPORTED.
  *   lse       may be NULL: the LSE store is skipped.
  *   stream    a hipStream_t (NULL = the null stream). Work is enqueued
  *             asynchronously; no entry point synchronises.
