@@ -59,6 +59,10 @@ def load_library():
         lib.attn_decode_num_splits.restype = I
         lib.attn_decode_splitk.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
         lib.attn_decode_splitk.restype = I
+        lib.attn_calib_mfma.argtypes = [I, I, P, P]
+        lib.attn_calib_mfma.restype = I
+        lib.attn_calib_read.argtypes = [P, S, P, I, P]
+        lib.attn_calib_read.restype = I
         lib.attn_strerror.argtypes = [I]
         lib.attn_strerror.restype = ctypes.c_char_p
         _lib = lib
@@ -190,3 +194,19 @@ def attn_decode(q, k_cache, v_cache, scale=None, window=0, num_splits=0,
                                       int(window), int(num_splits), _ptr(workspace),
                                       ctypes.c_size_t(workspace.numel()), _stream(q.device)))
     return out, lse
+
+
+def calib_mfma(blocks: int, iters: int, sink):
+    """Launch the bf16 matrix-core ceiling probe on the current stream."""
+    lib = load_library()
+    _check(lib.attn_calib_mfma(int(blocks), int(iters), _ptr(sink), _stream(sink.device)))
+    return blocks * 4 * iters * 8 * 32768
+
+
+def calib_read(buf, sink, blocks: int):
+    """Launch the streaming-read ceiling probe over tensor `buf`."""
+    lib = load_library()
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib.attn_calib_read(_ptr(buf), ctypes.c_size_t(nbytes), _ptr(sink), int(blocks),
+                               _stream(buf.device)))
+    return nbytes

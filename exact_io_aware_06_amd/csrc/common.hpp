@@ -93,6 +93,15 @@ __device__ __forceinline__ float swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
+// max(x, x of the lane 32 away) with v_permlane32_swap (no LDS round trip):
+// the swap of a register with itself returns, in its two results, this lane's
+// value and its partner's, in an order that max() does not care about.
+__device__ __forceinline__ float max_halves(float x) {
+  const unsigned u = __builtin_bit_cast(unsigned, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, (unsigned)r[0]), __builtin_bit_cast(float, (unsigned)r[1]));
+}
+
 __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;
 }

@@ -161,6 +161,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qp + ks * 16, qvalid));
   }
 
+  // LDS: K ring of two tiles at [0, 2 TILE), V ring of two tiles at
+  // [2 TILE, 4 TILE). K runs two tiles ahead of the softmax, V one tile.
+  constexpr int KRING = 0, VRING = 2 * T::TILE;
+
   // Per-lane LDS byte offsets, fixed for the whole kernel.
   // Q K^T operand: row kb*32 + l32, chunk 2 ks + g.
   uint32_t koff[T::KS];
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) {
         const int c = 4 * db + 2 * hh + (a >> 1);
-        voff[db][qh] = (uint32_t)(T::TILE + r * T::ROWB + ((c ^ sw) << 4) + (a & 1) * 8);
+        voff[db][qh] = (uint32_t)(r * T::ROWB + ((c ^ sw) << 4) + (a & 1) * 8);
       }
     }
   }
@@ -204,19 +208,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const uint16_t* vbase = p.v + head_kv * D;
   int loaded = 0, masked = 0;
 
-  // Issue the K and V DMA of key tile kt into pipeline stage stg.
-  auto issue = [&](int kt, int stg) {
+  // DMA of one K (or V) tile kt into the LDS slot at byte `slot`.
+  auto issue = [&](const uint16_t* base, int kt, int slot) {
     const long long k0 = (long long)kt * BN;
     const uint32_t bytes = k0 < p.Nk ? (uint32_t)((p.Nk - k0) * T::ROWB) : 0u;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(kbase + k0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(vbase + k0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * D, bytes);
 #pragma unroll
-    for (int i = 0; i < T::BPW; ++i) {
-      lds_u8* dst = L + stg * T::STAGE + (wave * T::BPW + i) * 1024;
-      dma16(rk, dst, dvoff[i]);
-      dma16(rv, dst + T::TILE, dvoff[i]);
-    }
-    if (COUNT) ++loaded;
+    for (int i = 0; i < T::BPW; ++i) dma16(rs, L + slot + (wave * T::BPW + i) * 1024, dvoff[i]);
   };
 
   // Does key tile kt need the per-element mask for any valid row here?
@@ -240,45 +238,49 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // fp32 P (for an LSE as accurate as fp32 allows).
   float l_b = 0.f, l_f = 0.f;
 
-  auto compute = [&](int kt, int stg) {
-    const lds_u8* st = L + stg * T::STAGE;
-    // S^T = K Q^T for this wave's 32 queries.
-    f32x16 sacc[T::KB];
+  // S^T = K Q^T of the K tile in ring slot kslot.
+  auto qk = [&](int kslot, f32x16 (&sacc)[T::KB]) {
+    const lds_u8* kt_lds = L + KRING + kslot * T::TILE;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
       sacc[kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < T::KS; ++ks)
-        sacc[kb] = mfma32x32x16(lds_b128(st, koff[ks] + kb * 32 * T::ROWB), qf[ks], sacc[kb]);
+        sacc[kb] = mfma32x32x16(lds_b128(kt_lds, koff[ks] + kb * 32 * T::ROWB), qf[ks], sacc[kb]);
     }
-    mfma_drain();
+  };
 
-    if (tile_partial(kt)) {
-      if (COUNT) ++masked;
-      // Key kt*BN + c + 4g is visible iff lo_q <= key <= hi_q; compare the
-      // compile-time offset c against the row's bounds relative to the tile.
-      const long long base = (long long)kt * BN + 4 * g;
-      const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
-      const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
+  // Boundary-tile mask, then this wave's row maxima of a score tile: returns
+  // the candidate reference max and whether it must replace m_ref.
+  auto mask_tile = [&](int kt, f32x16 (&sacc)[T::KB]) {
+    // Key kt*BN + c + 4g is visible iff lo_q <= key <= hi_q; compare the
+    // compile-time offset c against the row's bounds relative to the tile.
+    const long long base = (long long)kt * BN + 4 * g;
+    const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
+    const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
 #pragma unroll
-      for (int kb = 0; kb < T::KB; ++kb)
+    for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-          sacc[kb][r] = ((c >= rl) & (c <= rh)) ? sacc[kb][r] : -kInf;
-        }
-    }
-
-    // Row maximum over this tile (16 keys per register block, two halves).
+      for (int r = 0; r < 16; ++r) {
+        const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+        sacc[kb][r] = ((c >= rl) & (c <= rh)) ? sacc[kb][r] : -kInf;
+      }
+  };
+  auto row_max = [&](const f32x16 (&sacc)[T::KB]) -> float {
     float mx = -kInf;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = fmaxf(mx, swap_halves(mx));
+    return max_halves(mx);
+  };
+  // Move the reference maximum (and rescale O and the sums) if the new
+  // tile's maximum exceeds it by more than the threshold.
+  auto rescale = [&](float mx) {
     const float m_new = fmaxf(m_ref, mx);
     const bool need = m_new > m_ref + p.thr_raw;
     if (wave_any(need)) {
+      mfma_drain();  // O was last written by matrix-core instructions
       const float alpha = need ? fast_exp2((m_ref - m_new) * p.scale_log2) : 1.f;
       if (need) m_ref = m_new;
       l_b *= alpha;
@@ -286,9 +288,30 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < T::DB; ++i) oacc[i] *= alpha;
     }
+  };
+
+  // One pipelined step for key tile t, whose scores s_cur are already masked
+  // and whose maximum is already folded into m_ref:
+  //   DMA K(t+2), V(t+1);
+  //   block A: Q K^T of tile t+1 (matrix cores) beside exp / convert / sums of
+  //            tile t (vector ALU);
+  //   block B: O += P V of tile t beside mask and row max of tile t+1;
+  //   barrier, then the (rare) rescale for tile t+1.
+  // K(t+1) sits in ring slot kslot_next, V(t) in ring slot vslot. The last step
+  // computes a discarded extra score tile, which keeps both blocks free of
+  // branches; MASK_NEXT selects the boundary-tile variant of block B.
+  auto step = [&](int t, int kslot_next, int vslot, f32x16 (&s_cur)[T::KB],
+                  f32x16 (&s_nxt)[T::KB], bool mask_next) {
+    const int kt = kt_lo + t;
+    if (t + 2 < ntiles) {
+      issue(kbase, kt + 2, KRING + (1 - kslot_next) * T::TILE);
+      if (COUNT) ++loaded;
+    }
+    if (t + 1 < ntiles) issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
     const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
 
-    // P = exp2(s * scale * log2e - m), kept in registers as the B operand.
+    // Block A.
+    qk(kslot_next, s_nxt);
     bf16x8 pf[T::PS];
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
@@ -297,44 +320,57 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         f32x8 pv;
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          pv[i] = fast_exp2(__builtin_fmaf(sacc[kb][hf * 8 + i], p.scale_log2, -msub));
+          pv[i] = fast_exp2(__builtin_fmaf(s_cur[kb][hf * 8 + i], p.scale_log2, -msub));
         l_f += sum_f32x8(pv);
         pf[kb * 2 + hf] = to_bf16x8(pv);
         l_b = sum_bf16x8(pf[kb * 2 + hf], l_b);
       }
+    mfma_drain();  // s_nxt is read by the vector ALU below
 
-    // O^T += V^T P^T.
+    // Block B: O^T += V^T P^T.
+    const lds_u8* vt_lds = L + VRING + vslot * T::TILE;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-      for (int t = 0; t < T::PS; ++t) {
-        const uint2 lo = lds_tr_b64(st, voff[db][0] + t * 16 * T::ROWB);
-        const uint2 hi = lds_tr_b64(st, voff[db][1] + t * 16 * T::ROWB);
+      for (int tt = 0; tt < T::PS; ++tt) {
+        const uint2 lo = lds_tr_b64(vt_lds, voff[db][0] + tt * 16 * T::ROWB);
+        const uint2 hi = lds_tr_b64(vt_lds, voff[db][1] + tt * 16 * T::ROWB);
         const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[db] = mfma32x32x16(va, pf[t], oacc[db]);
+        oacc[db] = mfma32x32x16(va, pf[tt], oacc[db]);
       }
+    if (mask_next) {
+      if (COUNT) ++masked;
+      mask_tile(kt + 1, s_nxt);
+    }
+    const float mx = row_max(s_nxt);
+    wait_vmem();
+    __syncthreads();
+    if (t + 1 < ntiles) rescale(mx);
   };
 
-  // Two-stage pipeline: while tile i is computed from one stage, the DMA of
-  // tile i + 1 fills the other; one barrier per tile both publishes the new
-  // stage and retires the old one. Unrolled by two so stage offsets fold into
-  // instruction immediates.
+  f32x16 sA[T::KB], sB[T::KB];
   if (ntiles > 0) {
-    issue(kt_lo, 0);
-    wait_vmem();
-    __syncthreads();
-  }
-  for (int it = 0; it < ntiles; it += 2) {
-    if (it + 1 < ntiles) issue(kt_lo + it + 1, 1);
-    compute(kt_lo + it, 0);
-    wait_vmem();
-    __syncthreads();
-    if (it + 1 < ntiles) {
-      if (it + 2 < ntiles) issue(kt_lo + it + 2, 0);
-      compute(kt_lo + it + 1, 1);
-      wait_vmem();
-      __syncthreads();
+    issue(kbase, kt_lo, KRING);
+    issue(vbase, kt_lo, VRING);
+    if (COUNT) ++loaded;
+    if (ntiles > 1) {
+      issue(kbase, kt_lo + 1, KRING + T::TILE);
+      if (COUNT) ++loaded;
     }
+    wait_vmem();
+    __syncthreads();
+    qk(0, sA);
+    mfma_drain();
+    if (tile_partial(kt_lo)) {
+      if (COUNT) ++masked;
+      mask_tile(kt_lo, sA);
+    }
+    rescale(row_max(sA));
+    __syncthreads();  // K slot 0 is refilled by the first step
+  }
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, 1, 0, sA, sB, t + 1 < ntiles && tile_partial(kt_lo + t + 1));
+    if (t + 1 < ntiles) step(t + 1, 0, 1, sB, sA, t + 2 < ntiles && tile_partial(kt_lo + t + 2));
   }
   mfma_drain();
 

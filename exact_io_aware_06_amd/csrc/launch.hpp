@@ -43,6 +43,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(int B, int H, int d, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Ceiling probes (calib.hip).
+hipError_t launch_mfma_ceiling(int blocks, int iters, float* sink, hipStream_t stream);
+hipError_t launch_read_ceiling(const void* buf, size_t bytes, unsigned* sink, int blocks,
+                               hipStream_t stream);
+
 bool log_enabled();
 
 }  // namespace miattn

@@ -168,6 +168,23 @@ int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, 
   return launch_status(miattn::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_calib_mfma(int blocks, int iters, float* sink, void* stream) {
+  if (blocks < 1 || iters < 1 || sink == nullptr) return MIATTN_EINVAL;
+  int st = device_status();
+  if (st != MIATTN_OK) return st;
+  return launch_status(
+      miattn::launch_mfma_ceiling(blocks, iters, sink, static_cast<hipStream_t>(stream)));
+}
+
+int attn_calib_read(const void* buf, size_t bytes, unsigned* sink, int blocks, void* stream) {
+  if (buf == nullptr || sink == nullptr || bytes == 0 || bytes % 16 != 0 || blocks < 1)
+    return MIATTN_EINVAL;
+  int st = device_status();
+  if (st != MIATTN_OK) return st;
+  return launch_status(
+      miattn::launch_read_ceiling(buf, bytes, sink, blocks, static_cast<hipStream_t>(stream)));
+}
+
 const char* attn_strerror(int status) {
   switch (status) {
     case MIATTN_OK: return "success";

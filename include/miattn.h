@@ -135,6 +135,20 @@ int attn_fwd_tile_counts(const void* q, const void* k, const void* v, void* o, f
                          int B, int H, int Hkv, int Nq, int Nk, int d,
                          float scale, int causal, int window, int* counts, void* stream);
 
+/*
+ * Ceiling probes (they compute no attention): the rates this device sustains,
+ * reported next to the published peaks when pricing the kernels above.
+ * attn_calib_mfma: `blocks` work-groups of 4 waves, each wave issuing
+ *   iters x 8 independent bf16 32x32x16 matrix instructions;
+ *   FLOPs = blocks * 4 * iters * 8 * 32768. sink: device float[blocks]
+ *   (written only in a practically unreachable case).
+ * attn_calib_read: streams `bytes` (a multiple of 16) from device buffer
+ *   `buf` once with 16-byte loads over `blocks` work-groups of 256 threads.
+ *   sink: device unsigned[1].
+ */
+int attn_calib_mfma(int blocks, int iters, float* sink, void* stream);
+int attn_calib_read(const void* buf, size_t bytes, unsigned* sink, int blocks, void* stream);
+
 /* Static string for a status code. */
 const char* attn_strerror(int status);
 
