@@ -38,6 +38,12 @@ __device__ __forceinline__ uint2 lds_tr_b64(const lds_u8* base, uint32_t off) {
   return __builtin_bit_cast(uint2, r);
 }
 
+// 8-byte LDS store at a byte offset.
+__device__ __forceinline__ void lds_st_b64(lds_u8* base, uint32_t off, uint2 v) {
+  typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+  *(__attribute__((address_space(3))) u32x2*)(base + off) = u32x2{v.x, v.y};
+}
+
 // Raw buffer resource over [base, base + bytes): loads past the end read 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);

@@ -67,7 +67,7 @@ struct FwdParams {
 
 template <int D>
 struct Tile {
-  static constexpr int BN = (D == 128) ? 64 : 128;  // keys per K/V tile
+  static constexpr int BN = 64;                      // keys per K/V tile
   static constexpr int ROWB = D * 2;                 // bytes per K/V row
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int RPB = 64 / CPR;               // rows per 1 KB DMA block
@@ -438,7 +438,7 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.counts = a.counts;
   if (log_enabled())
     fprintf(stderr, "[miattn] fwd_bf16 d=%d grid=%lld block=%d BM=%d BN=%d xcd_remap=%d\n", a.d,
-            (long long)a.B * a.H * p.nqt, kThreads, kBM, a.d == 128 ? 64 : 128, p.xcd_remap);
+            (long long)a.B * a.H * p.nqt, kThreads, kBM, Tile<128>::BN, p.xcd_remap);
   const bool count = a.counts != nullptr;
   return a.d == 128 ? launch_d<128>(p, stream, count) : launch_d<64>(p, stream, count);
 }
