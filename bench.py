@@ -134,7 +134,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
-    ap.add_argument("--cpu-seqs", type=int, default=16)
+    ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32"], default="all",
                     help="launch only one part of the step (for profiling runs)")
     ap.add_argument("--no-ceilings", action="store_true",
