@@ -21,6 +21,8 @@ Modules:
   online     - the pages' online-softmax recurrence and the split-K merge, as
                independent fp64 models used only to pin the definition
   tiles      - which (query-tile, key-tile) blocks hold any visible pair
+  varlen     - packed documents (block-diagonal mask) and decode over caches
+               of per-sequence length
 """
 
 from .attention import (  # noqa: F401
@@ -33,3 +35,10 @@ from .attention import (  # noqa: F401
 )
 from .online import online_softmax_model, split_partials_ref, merge_ref  # noqa: F401
 from .tiles import tiles_needed  # noqa: F401
+from .varlen import (  # noqa: F401
+    packed_visible_mask,
+    attention_varlen_ref,
+    attention_varlen_rows_ref,
+    decode_kvlens_ref,
+    decode_kvlens_rows_ref,
+)

@@ -150,3 +150,96 @@ def decode_inputs(cfg: DecodeConfig, seed: int, device="cpu", batches=None):
         kc[i] = gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_K, b, cfg.dtype, 1.0, device)
         vc[i] = gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_V, b, cfg.dtype, 1.0, device)
     return q, kc, vc
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length sequences and per-sequence KV-cache lengths.
+#
+# Lengths come from numpy generators seeded with seed_key(seed, TID_LEN, unit),
+# one per training context (packed prefill) or one per batch (decode), so the
+# length mix is fixed by the seed alone.
+
+TID_LEN = 3
+
+
+def packed_lengths(seed: int, contexts: int, context_len: int, min_len: int,
+                   max_len: int) -> list:
+    """Document lengths filling ``contexts`` training contexts of ``context_len`` tokens.
+
+    Each context is filled with documents whose lengths are drawn
+    log-uniformly in [min_len, max_len] (rounded down to an integer); the
+    document that would run past the end of the context is cut there, so no
+    document spans two contexts and every context holds exactly
+    ``context_len`` tokens.
+    """
+    out = []
+    for c in range(contexts):
+        rng = np.random.default_rng(seed_key(seed, TID_LEN, c))
+        left = context_len
+        while left > 0:
+            n = int(math.exp(rng.uniform(math.log(min_len), math.log(max_len + 1))))
+            n = max(1, min(n, max_len, left))
+            out.append(n)
+            left -= n
+    return out
+
+
+def cu_seqlens(lengths) -> np.ndarray:
+    """int32 offsets [len(lengths) + 1]: 0, then the running totals."""
+    cu = np.zeros(len(lengths) + 1, dtype=np.int64)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    return cu.astype(np.int32)
+
+
+def kv_lengths(seed: int, B: int, Nk: int, lo: int = 1) -> np.ndarray:
+    """int32 [B]: per-sequence cache lengths, uniform integers in [lo, Nk]."""
+    rng = np.random.default_rng(seed_key(seed, TID_LEN, 0))
+    return rng.integers(lo, Nk + 1, size=B).astype(np.int32)
+
+
+@dataclass(frozen=True)
+class PackedConfig:
+    name: str
+    H: int
+    Hkv: int
+    d: int
+    contexts: int       # training contexts, each packed with documents
+    context_len: int    # tokens per context
+    min_len: int        # document length range (log-uniform)
+    max_len: int
+    causal: int
+    window: int
+    scale: float
+    dtype: str = "bf16"
+    note: str = ""
+
+    def with_(self, **kw) -> "PackedConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return PackedConfig(**d)
+
+    def lengths(self, seed: int) -> list:
+        return packed_lengths(seed, self.contexts, self.context_len, self.min_len,
+                              self.max_len)
+
+
+# Packed prefill: four 8k training contexts ("What Lost, and Why": 2k-8k
+# training contexts) each filled with documents of log-uniform length in
+# [64, 8192], causal, the GQA head shape of the prefill workloads.
+PACKED = {
+    "p1": PackedConfig("p1", 32, 8, 128, 4, 8192, 64, 8192, 1, 0,
+                       _f32(1 / math.sqrt(128)),
+                       note="packed causal GQA prefill, 4 x 8k contexts, log-uniform documents"),
+}
+
+# Decode over caches of mixed length: the decode workload's shapes with each
+# sequence holding a uniform random number of keys in [1, 32768].
+DECODE_KVLENS = CONFIGS["c5"].with_(name="k1", note="split-K decode, per-sequence cache lengths")
+
+
+def packed_inputs(cfg: PackedConfig, total_q: int, total_k: int, seed: int, device="cpu"):
+    """(q, k, v) packed: q [H, total_q, d], k/v [Hkv, total_k, d]."""
+    q = gen_normal((cfg.H, total_q, cfg.d), seed, TID_Q, 0, cfg.dtype, 1.0, device)
+    k = gen_normal((cfg.Hkv, total_k, cfg.d), seed, TID_K, 0, cfg.dtype, 1.0, device)
+    v = gen_normal((cfg.Hkv, total_k, cfg.d), seed, TID_V, 0, cfg.dtype, 1.0, device)
+    return q, k, v
