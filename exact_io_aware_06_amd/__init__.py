@@ -9,9 +9,12 @@ the first call does, and raises if it has not been built.
 from .api import (  # noqa: F401
     MiattnError,
     attn_fwd,
+    attn_fwd_varlen,
     attn_decode,
+    attn_decode_varlen,
     decode_workspace_bytes,
     fwd_tile_counts,
+    fwd_varlen_tile_counts,
     fwd_tile_shape,
     library_path,
     load_library,

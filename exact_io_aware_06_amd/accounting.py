@@ -80,3 +80,31 @@ def decode_bytes(B, H, Hkv, Nk, d, elem_bytes=2, window=0, lse=True) -> int:
 def decode_flops(B, H, Nk, d, window=0) -> int:
     keys = Nk if window <= 0 else min(Nk, window + 1)
     return 4 * d * keys * B * H
+
+
+def packed_visible_pairs(cu_q, cu_k, causal: bool, window: int) -> int:
+    """Visible (query, key) pairs of one head over packed documents.
+
+    The mask is block-diagonal by document ("What Lost, and Why", closing
+    section: the mask restarts at each document boundary), so the count is
+    the sum of each document's own count.
+    """
+    total = 0
+    for e in range(len(cu_q) - 1):
+        total += visible_pairs(int(cu_q[e + 1]) - int(cu_q[e]), int(cu_k[e + 1]) - int(cu_k[e]),
+                               causal, window)
+    return total
+
+
+def packed_flops(H: int, cu_q, cu_k, d: int, causal: bool, window: int) -> int:
+    """Algorithmic FLOPs of one packed forward call: 4 d per visible pair per head."""
+    return 4 * d * H * packed_visible_pairs(cu_q, cu_k, causal, window)
+
+
+def decode_kvlens_bytes(H, Hkv, kv_lens, d, elem_bytes=2, window=0, lse=True) -> int:
+    """Compulsory bytes of one decode step over caches of per-sequence length."""
+    keys = sum(int(n) if window <= 0 else min(int(n), window + 1) for n in kv_lens)
+    B = len(kv_lens)
+    kv = 2 * Hkv * keys * d * elem_bytes
+    qo = 2 * B * H * d * elem_bytes
+    return kv + qo + (B * H * 4 if lse else 0)

@@ -51,6 +51,14 @@ def load_library():
         lib.attn_fwd_f32.restype = I
         lib.attn_fwd_tile_counts.argtypes = fwd_args[:-1] + [P, P]
         lib.attn_fwd_tile_counts.restype = I
+        varlen_args = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I]
+        lib.attn_fwd_varlen.argtypes = varlen_args + [P]
+        lib.attn_fwd_varlen.restype = I
+        lib.attn_fwd_varlen_tile_counts.argtypes = varlen_args + [P, P]
+        lib.attn_fwd_varlen_tile_counts.restype = I
+        lib.attn_decode_splitk_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P,
+                                                  S, P]
+        lib.attn_decode_splitk_varlen.restype = I
         lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
         lib.attn_fwd_tile_shape.restype = I
         lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -157,6 +165,76 @@ def fwd_tile_counts(q, k, v, scale=None, causal=False, window=0):
     return out, lse, counts
 
 
+def _varlen_checks(q, k, v, cu_seqlens_q, cu_seqlens_k):
+    import torch
+    _require(q.dim() == 3 and k.dim() == 3 and v.shape == k.shape,
+             "packed q [H, total_q, d], k/v [Hkv, total_k, d]")
+    _require(q.is_cuda and k.device == q.device and v.device == q.device,
+             "q, k, v must be on the same GPU")
+    _require(q.dtype == torch.bfloat16 and k.dtype == q.dtype and v.dtype == q.dtype,
+             "packed attention takes bfloat16")
+    _require(q.is_contiguous() and k.is_contiguous() and v.is_contiguous(),
+             "q, k, v must be contiguous")
+    _require(k.shape[2] == q.shape[2], "head dims differ")
+    for cu in (cu_seqlens_q, cu_seqlens_k):
+        _require(cu.dim() == 1 and cu.dtype == torch.int32 and cu.device == q.device
+                 and cu.is_contiguous(), "cu_seqlens must be contiguous int32 on q's GPU")
+    _require(cu_seqlens_q.numel() == cu_seqlens_k.numel() and cu_seqlens_q.numel() >= 1,
+             "cu_seqlens_q and cu_seqlens_k must both hold num_seqs + 1 offsets")
+    H, total_q, d = q.shape
+    return H, k.shape[0], total_q, k.shape[1], d, cu_seqlens_q.numel() - 1
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
+                    causal=False, window=0, out=None, lse=None):
+    """Packed documents: q [H, total_q, d], k/v [Hkv, total_k, d] bf16.
+
+    cu_seqlens_* are device int32 offsets [num_seqs + 1]; max_seqlen_q bounds
+    every document's query count. Returns (O like q, LSE [H, total_q] fp32).
+    """
+    import torch
+    H, Hkv, total_q, total_k, d, ns = _varlen_checks(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
+    _require(lse.shape == (H, total_q) and lse.dtype == torch.float32 and lse.is_contiguous(),
+             "bad lse")
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
+                                   _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), ns, H, Hkv, total_q,
+                                   total_k, int(max_seqlen_q), d, ctypes.c_float(scale),
+                                   int(bool(causal)), int(window), _stream(q.device)))
+    return out, lse
+
+
+def fwd_varlen_tile_counts(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
+                           causal=False, window=0):
+    """attn_fwd_varlen plus per-work-group (tiles loaded, tiles masked) counts.
+
+    Returns (O, LSE, counts [num_seqs, H, ceil(max_seqlen_q / BM), 2] int32).
+    """
+    import torch
+    H, Hkv, total_q, total_k, d, ns = _varlen_checks(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    bm, _ = fwd_tile_shape(d, False)
+    nqt = -(-int(max_seqlen_q) // bm)
+    out = torch.empty_like(q)
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
+    counts = torch.full((ns, H, nqt, 2), -1, dtype=torch.int32, device=q.device)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.attn_fwd_varlen_tile_counts(
+            _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(cu_seqlens_q),
+            _ptr(cu_seqlens_k), ns, H, Hkv, total_q, total_k, int(max_seqlen_q), d,
+            ctypes.c_float(scale), int(bool(causal)), int(window), _ptr(counts),
+            _stream(q.device)))
+    return out, lse, counts
+
+
 def decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits=0) -> int:
     return int(load_library().attn_decode_workspace_bytes(B, H, Hkv, Nk, d, num_splits))
 
@@ -193,6 +271,46 @@ def attn_decode(q, k_cache, v_cache, scale=None, window=0, num_splits=0,
                                       _ptr(lse), B, H, Hkv, Nk, d, ctypes.c_float(scale),
                                       int(window), int(num_splits), _ptr(workspace),
                                       ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+    return out, lse
+
+
+def attn_decode_varlen(q, k_cache, v_cache, kv_lens, scale=None, window=0, num_splits=0,
+                       out=None, lse=None, workspace=None):
+    """Split-K decode where sequence b holds kv_lens[b] keys (device int32 [B]).
+
+    q [B,H,d], caches [B,Hkv,Nk,d] bf16. Returns (O [B,H,d] bf16, LSE [B,H] fp32).
+    """
+    import torch
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
+             "q [B,H,d], caches [B,Hkv,Nk,d]")
+    _require(q.is_cuda and k_cache.device == q.device and v_cache.device == q.device,
+             "tensors must be on the same GPU")
+    _require(q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16
+             and v_cache.dtype == torch.bfloat16, "decode takes bfloat16")
+    _require(q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous(),
+             "tensors must be contiguous")
+    B, H, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    _require(k_cache.shape[0] == B and k_cache.shape[3] == d, "cache shape mismatch")
+    _require(kv_lens.shape == (B,) and kv_lens.dtype == torch.int32
+             and kv_lens.device == q.device and kv_lens.is_contiguous(),
+             "kv_lens must be contiguous int32 [B] on q's GPU")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    nbytes = int(lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_decode_splitk_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                             _ptr(kv_lens), _ptr(out), _ptr(lse), B, H, Hkv, Nk,
+                                             d, ctypes.c_float(scale), int(window),
+                                             int(num_splits), _ptr(workspace),
+                                             ctypes.c_size_t(workspace.numel()),
+                                             _stream(q.device)))
     return out, lse
 
 

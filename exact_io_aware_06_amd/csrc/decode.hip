@@ -4,7 +4,8 @@
 // Decode is bound by reading the KV cache once per step ("Attention
 // Research", section 1; "Quadratic Complexity Bottleneck", KV cache entry).
 // Split-K over keys ("Attention Research", section 2) gives the GPU enough
-// independent work: the key range of each sequence is cut into S contiguous
+// independent work: the key range of each sequence (all Nk cache rows, or its
+// own length when lengths differ per sequence) is cut into S contiguous
 // chunks, and each (sequence, KV head, chunk) becomes one work-group that
 // reads its K/V rows exactly once for all G query heads sharing that KV head.
 //
@@ -20,7 +21,6 @@
 // O = sum_s exp(lse_s - LSE) O_s; chunks with no visible key have
 // lse_s = -inf and weigh nothing.
 
-#include <algorithm>
 #include <cstdio>
 
 #include "common.hpp"
@@ -40,9 +40,10 @@ struct SplitParams {
   const uint16_t* v;
   float* o_s;
   float* lse_s;
-  int B, H, Hkv, Nk, G, S, C;
-  int vis_lo;  // first visible key (window), else 0
+  int B, H, Hkv, Nk, G, S;
+  int window;
   float scale, scale_log2, thr_raw;
+  const int* kv_lens;  // per-sequence key counts, or null (all Nk)
 };
 
 struct MergeParams {
@@ -80,9 +81,14 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   const int bk = blockIdx.x / p.S;
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
 
-  const int lo = min(p.Nk, s * p.C);
-  const int hi = min(p.Nk, lo + p.C);
-  const int start = max(lo, p.vis_lo);
+  // This sequence's keys (its first n cache rows; the query sits at n - 1),
+  // cut into S chunks of C = ceil(n / S); the window keeps the last W + 1.
+  const int n = p.kv_lens != nullptr ? min(max(p.kv_lens[b], 0), p.Nk) : p.Nk;
+  const int C = (n + p.S - 1) / p.S;
+  const int vis_lo = p.window > 0 ? max(0, n - 1 - p.window) : 0;
+  const int lo = min(n, s * C);
+  const int hi = min(n, lo + C);
+  const int start = max(lo, vis_lo);
   const int ntiles = hi > start ? (hi - start + kBN - 1) / kBN : 0;
 
   // Query heads of this group as the B-operand columns.
@@ -302,15 +308,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.Nk = a.Nk;
   sp.G = a.H / a.Hkv;
   sp.S = a.splits;
-  sp.C = (a.Nk + a.splits - 1) / a.splits;
-  sp.vis_lo = a.window > 0 ? (int)std::max(0LL, (long long)a.Nk - 1 - a.window) : 0;
+  sp.window = a.window;
+  sp.kv_lens = a.kv_lens;
   sp.scale = a.scale;
   sp.scale_log2 = a.scale * kLog2e;
   sp.thr_raw = kRescaleThreshold / sp.scale_log2;
   const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * a.splits);
   if (log_enabled())
-    fprintf(stderr, "[miattn] decode d=%d splits=%d chunk=%d split_grid=%u merge_grid=%d\n", a.d,
-            a.splits, sp.C, nsplit_blk, a.B * a.H);
+    fprintf(stderr, "[miattn] decode d=%d splits=%d kv_lens=%s split_grid=%u merge_grid=%d\n",
+            a.d, a.splits, a.kv_lens != nullptr ? "per-sequence" : "uniform", nsplit_blk,
+            a.B * a.H);
   void* sargs[] = {&sp};
   const void* sfn = a.d == 128 ? reinterpret_cast<const void*>(&decode_split_kernel<128>)
                                : reinterpret_cast<const void*>(&decode_split_kernel<64>);

@@ -15,9 +15,10 @@
 // that row sit in the lane 32 apart. The row max and row sum are in-lane
 // reductions plus a single exchange between the two wave halves. The same
 // registers, rounded to bf16, are directly the B operand of O^T += V^T P^T,
-// so P never leaves the registers. V is staged into LDS transposed (dims as
-// rows) with the key order the P registers imply, so each lane reads its V^T
-// operand with one 16-byte LDS read.
+// so P never leaves the registers. K and V tiles are copied row-major from
+// device memory into LDS by direct global-to-LDS loads; each lane gathers its
+// V^T operand from the row-major V tile with two transposing LDS reads
+// (ds_read_b64_tr_b16), in the key order its P registers hold.
 //
 // Online softmax (the pages' running max and running denominator, rescaling
 // the partial output when the maximum grows) is done lazily: the reference
@@ -26,6 +27,13 @@
 // LSE = m + ln l are identical in exact arithmetic for any reference value;
 // bounding the growth keeps P <= 256, far from fp32/bf16 overflow, and skips
 // most of the rescaling multiplies.
+//
+// Packed documents ("What Lost, and Why", closing section: the mask restarts
+// at every document boundary) reuse the same kernel: the batch index becomes
+// the document index, whose query and key rows are located through row
+// offsets, and each document is masked as a sequence of its own. The grid
+// then covers ceil(max document length / BM) query tiles per document and the
+// tiles past a document's end exit at once.
 //
 // Work decomposition: grid = B * H * ceil(Nq / BM) work-groups, the query
 // tiles with the most visible keys first (causal), and when (B * Hkv) is a
@@ -63,6 +71,8 @@ struct FwdParams {
   int nqt;
   int xcd_remap;
   int* counts;
+  const int* cu_q;  // packed documents: row offsets, or null
+  const int* cu_k;
 };
 
 template <int D>
@@ -132,12 +142,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   decode_workgroup(p, blockIdx.x, b, h, qt);
   const int kvh = h / p.G;
   const int q0 = qt * kBM;
-  const int off = p.Nk - p.Nq;
-  const int q_last = min(q0 + kBM, p.Nq) - 1;
+
+  // Rows of this (batch, head): Nq queries from row head_q, Nk keys from row
+  // head_kv. For packed documents b is the document, whose rows start at its
+  // offsets within each head's packed sequence; a document whose offsets are
+  // out of order or out of range is treated as empty.
+  int Nq = p.Nq, Nk = p.Nk;
+  size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+  size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
+  if (p.cu_q != nullptr) {
+    const int qs = p.cu_q[b], qe = p.cu_q[b + 1];
+    const int ks = p.cu_k[b], ke = p.cu_k[b + 1];
+    const bool ok = 0 <= qs && qs <= qe && qe <= p.Nq && 0 <= ks && ks <= ke && ke <= p.Nk;
+    Nq = ok ? qe - qs : 0;
+    Nk = ok ? ke - ks : 0;
+    head_q = (size_t)h * p.Nq + (ok ? qs : 0);
+    head_kv = (size_t)kvh * p.Nk + (ok ? ks : 0);
+  }
+  if (q0 >= Nq) {  // a query tile past the end of its document: nothing to do
+    if (COUNT && threadIdx.x == 0) {
+      int* c = p.counts + 2 * ((size_t)(b * p.H + h) * p.nqt + qt);
+      c[0] = 0;
+      c[1] = 0;
+    }
+    return;
+  }
+  const int off = Nk - Nq;
+  const int q_last = min(q0 + kBM, Nq) - 1;
   const long long p_lo = (long long)q0 + off, p_hi = (long long)q_last + off;
 
   // Key range visible to any row of this work-group.
-  long long key_lo = 0, key_hi = p.Nk;  // [key_lo, key_hi)
+  long long key_lo = 0, key_hi = Nk;  // [key_lo, key_hi)
   if (p.causal) key_hi = min(key_hi, p_hi + 1);
   else if (p.window > 0) key_hi = min(key_hi, p_hi + p.window + 1);
   if (p.window > 0) key_lo = max(key_lo, p_lo - p.window);
@@ -147,13 +182,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // This lane's query row and its Q fragments (B operand of S^T = K Q^T).
   const int qrow = q0 + wave * 32 + l32;
-  const bool qvalid = qrow < p.Nq;
+  const bool qvalid = qrow < Nq;
   const long long qpos = (long long)qrow + off;
   // Keys this row may see: [lo_q, hi_q] (used on boundary tiles only).
   const long long lo_q = p.window > 0 ? qpos - p.window : 0;
-  long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)p.Nk - 1);
-  hi_q = min(hi_q, (long long)p.Nk - 1);
-  const size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+  long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)Nk - 1);
+  hi_q = min(hi_q, (long long)Nk - 1);
   bf16x8 qf[T::KS];
   {
     const uint16_t* qp = p.q + (head_q + (qvalid ? qrow : 0)) * D + g * 8;
@@ -203,7 +237,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     dvoff[i] = (uint32_t)(r * T::ROWB + (((lane % T::CPR) ^ swz<D>(r)) << 4));
   }
 
-  const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
   const uint16_t* kbase = p.k + head_kv * D;
   const uint16_t* vbase = p.v + head_kv * D;
   int loaded = 0, masked = 0;
@@ -211,7 +244,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // DMA of one K (or V) tile kt into the LDS slot at byte `slot`.
   auto issue = [&](const uint16_t* base, int kt, int slot) {
     const long long k0 = (long long)kt * BN;
-    const uint32_t bytes = k0 < p.Nk ? (uint32_t)((p.Nk - k0) * T::ROWB) : 0u;
+    const uint32_t bytes = k0 < Nk ? (uint32_t)((Nk - k0) * T::ROWB) : 0u;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * D, bytes);
 #pragma unroll
     for (int i = 0; i < T::BPW; ++i) dma16(rs, L + slot + (wave * T::BPW + i) * 1024, dvoff[i]);
@@ -220,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   // Does key tile kt need the per-element mask for any valid row here?
   auto tile_partial = [&](int kt) -> bool {
     const long long k0 = (long long)kt * BN, k1 = k0 + BN - 1;
-    if (k1 >= p.Nk) return true;
+    if (k1 >= Nk) return true;
     if (p.causal && k1 > p_lo) return true;
     if (p.window > 0) {
       if (k0 < p_hi - p.window) return true;
@@ -433,7 +466,9 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.thr_raw = kRescaleThreshold / p.scale_log2;
   p.causal = a.causal;
   p.window = a.window;
-  p.nqt = (a.Nq + kBM - 1) / kBM;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
+  p.nqt = ((a.cu_q != nullptr ? a.max_q : a.Nq) + kBM - 1) / kBM;
   p.xcd_remap = ((a.B * a.Hkv) % 8 == 0) ? 1 : 0;
   p.counts = a.counts;
   if (log_enabled())

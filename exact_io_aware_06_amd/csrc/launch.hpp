@@ -17,6 +17,13 @@ struct FwdArgs {
   float scale;
   int causal, window;
   int* counts;  // optional per-work-group (tiles loaded, tiles masked)
+  // Packed documents (null for fixed-length calls): B documents whose query
+  // and key rows are [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]) of one
+  // packed sequence of Nq query rows and Nk key rows; max_q is at least every
+  // document's query count.
+  const int* cu_q;
+  const int* cu_k;
+  int max_q;
 };
 
 struct DecodeArgs {
@@ -30,6 +37,8 @@ struct DecodeArgs {
   int window;
   int splits;
   void* workspace;
+  // Per-sequence cache lengths in [0, Nk] (null: every sequence holds Nk keys).
+  const int* kv_lens;
 };
 
 // Query-tile rows / key-tile columns of the bf16 and fp32 forward kernels.

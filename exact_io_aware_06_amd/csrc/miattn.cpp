@@ -84,6 +84,33 @@ int run_fwd(bool f32, const void* q, const void* k, const void* v, void* o, floa
   return launch_status(f32 ? miattn::launch_fwd_f32(a, s) : miattn::launch_fwd_bf16(a, s));
 }
 
+// Packed documents: same checks as check_fwd, on the packed sizes.
+int run_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                   const int* cu_q, const int* cu_k, int num_seqs, int H, int Hkv, int total_q,
+                   int total_k, int max_q, int d, float scale, int causal, int window,
+                   int* counts, void* stream) {
+  if (num_seqs < 0 || H < 1 || Hkv < 1 || total_q < 0 || total_k < 0 || max_q < 0)
+    return MIATTN_EINVAL;
+  if (H % Hkv != 0) return MIATTN_EINVAL;
+  if (causal != 0 && causal != 1) return MIATTN_EINVAL;
+  if (window < 0 || !valid_scale(scale)) return MIATTN_EINVAL;
+  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
+  if (num_seqs > 0 && (cu_q == nullptr || cu_k == nullptr)) return MIATTN_EINVAL;
+  if (total_q > 0 && (q == nullptr || o == nullptr)) return MIATTN_EINVAL;
+  if (total_q > 0 && total_k > 0 && (k == nullptr || v == nullptr)) return MIATTN_EINVAL;
+  int bm = 0, bn = 0;
+  miattn::fwd_bf16_tile_shape(d, &bm, &bn);
+  const long long nqt = ((long long)max_q + bm - 1) / bm;
+  if ((long long)num_seqs * H * nqt > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  if ((long long)total_k * d * 4 > 0xFFFFFFFFLL) return MIATTN_EUNSUPPORTED;
+  if (num_seqs == 0 || max_q == 0 || total_q == 0) return MIATTN_OK;
+  int st = device_status();
+  if (st != MIATTN_OK) return st;
+  FwdArgs a{q,     k,      v,      o,      lse,  num_seqs, H,    Hkv,  total_q,
+            total_k, d, scale, causal, window, counts, cu_q,     cu_k, max_q};
+  return launch_status(miattn::launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 int resolve_splits(int B, int Hkv, int Nk, int num_splits) {
   if (B < 0 || Hkv < 1 || Nk < 0 || num_splits < 0) return MIATTN_EINVAL;
   if (num_splits > 0) {
@@ -100,6 +127,31 @@ int resolve_splits(int B, int Hkv, int Nk, int num_splits) {
   if (want > cap) want = cap;
   if (want < 1) want = 1;
   return (int)want;
+}
+
+int run_decode(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
+               void* o, float* lse, int B, int H, int Hkv, int Nk, int d, float scale,
+               int window, int num_splits, void* workspace, size_t workspace_bytes,
+               void* stream) {
+  if (B < 0 || H < 1 || Hkv < 1 || Nk < 0) return MIATTN_EINVAL;
+  if (H % Hkv != 0) return MIATTN_EINVAL;
+  if (window < 0 || !valid_scale(scale)) return MIATTN_EINVAL;
+  const int S = resolve_splits(B, Hkv, Nk, num_splits);
+  if (S < 0) return S;
+  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
+  if (H / Hkv > 32) return MIATTN_EUNSUPPORTED;
+  if ((long long)B * Hkv * S > (long long)INT_MAX || (long long)B * H > (long long)INT_MAX)
+    return MIATTN_EUNSUPPORTED;
+  if (B == 0) return MIATTN_OK;
+  if (q == nullptr || o == nullptr) return MIATTN_EINVAL;
+  if (Nk > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
+  const size_t need = miattn::decode_workspace_bytes(B, H, d, S);
+  if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
+  int st = device_status();
+  if (st != MIATTN_OK) return st;
+  DecodeArgs a{q,     k_cache, v_cache, o, lse,       B,      H,
+               Hkv,   Nk,      d,       scale, window, S, workspace, kv_lens};
+  return launch_status(miattn::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -148,24 +200,35 @@ size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num
 int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, void* o,
                        float* lse, int B, int H, int Hkv, int Nk, int d, float scale, int window,
                        int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
-  if (B < 0 || H < 1 || Hkv < 1 || Nk < 0) return MIATTN_EINVAL;
-  if (H % Hkv != 0) return MIATTN_EINVAL;
-  if (window < 0 || !valid_scale(scale)) return MIATTN_EINVAL;
-  const int S = resolve_splits(B, Hkv, Nk, num_splits);
-  if (S < 0) return S;
-  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
-  if (H / Hkv > 32) return MIATTN_EUNSUPPORTED;
-  if ((long long)B * Hkv * S > (long long)INT_MAX || (long long)B * H > (long long)INT_MAX)
-    return MIATTN_EUNSUPPORTED;
-  if (B == 0) return MIATTN_OK;
-  if (q == nullptr || o == nullptr) return MIATTN_EINVAL;
-  if (Nk > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
-  const size_t need = miattn::decode_workspace_bytes(B, H, d, S);
-  if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
-  int st = device_status();
-  if (st != MIATTN_OK) return st;
-  DecodeArgs a{q, k_cache, v_cache, o, lse, B, H, Hkv, Nk, d, scale, window, S, workspace};
-  return launch_status(miattn::launch_decode(a, static_cast<hipStream_t>(stream)));
+  return run_decode(q, k_cache, v_cache, nullptr, o, lse, B, H, Hkv, Nk, d, scale, window,
+                    num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int* kv_lens, void* o, float* lse, int B, int H, int Hkv,
+                              int Nk, int d, float scale, int window, int num_splits,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (B > 0 && kv_lens == nullptr) return MIATTN_EINVAL;
+  return run_decode(q, k_cache, v_cache, kv_lens, o, lse, B, H, Hkv, Nk, d, scale, window,
+                    num_splits, workspace, workspace_bytes, stream);
+}
+
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int H,
+                    int Hkv, int total_q, int total_k, int max_seqlen_q, int d, float scale,
+                    int causal, int window, void* stream) {
+  return run_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, H, Hkv, total_q,
+                        total_k, max_seqlen_q, d, scale, causal, window, nullptr, stream);
+}
+
+int attn_fwd_varlen_tile_counts(const void* q, const void* k, const void* v, void* o,
+                                float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                                int num_seqs, int H, int Hkv, int total_q, int total_k,
+                                int max_seqlen_q, int d, float scale, int causal, int window,
+                                int* counts, void* stream) {
+  if (counts == nullptr && (long long)num_seqs * H * max_seqlen_q > 0) return MIATTN_EINVAL;
+  return run_fwd_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, num_seqs, H, Hkv, total_q,
+                        total_k, max_seqlen_q, d, scale, causal, window, counts, stream);
 }
 
 int attn_calib_mfma(int blocks, int iters, float* sink, void* stream) {

@@ -91,6 +91,38 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  float scale, int causal, int window, void* stream);
 
 /*
+ * Packed variable-length documents, bfloat16 in and out, fp32 LSE. Several
+ * documents are packed along one token axis; the mask restarts at every
+ * document boundary, so no row sees another document ("What Lost, and Why",
+ * closing section: masking across packed documents is the silent bug to
+ * avoid). Each document is attended exactly as attn_fwd attends one sequence:
+ * bottom-right causal alignment and the window counted from the document's
+ * own start, GQA as above.
+ *
+ * Layout: q, o [H, total_q, d]; k, v [Hkv, total_k, d]; lse [H, total_q] fp32
+ * or NULL (the fixed-length layout with B = 1 and the documents end to end).
+ * cu_seqlens_q, cu_seqlens_k: DEVICE int32 arrays of num_seqs + 1 offsets,
+ * non-decreasing from 0 to total_q (resp. total_k); document e owns query
+ * rows [cu_seqlens_q[e], cu_seqlens_q[e+1]) and key rows
+ * [cu_seqlens_k[e], cu_seqlens_k[e+1]). Documents may be empty; one with
+ * queries but no keys gets O = 0, LSE = -inf.
+ * max_seqlen_q: a host-side bound, at least every document's query count; it
+ * sizes the grid (num_seqs * H * ceil(max_seqlen_q / block_m) work-groups,
+ * those past a document's end exit at once).
+ *
+ * Errors: host-visible arguments are validated as for attn_fwd (and the
+ * offset arrays must be non-NULL when num_seqs > 0). The offsets live on the
+ * device and are not read by the host: a document whose offsets are out of
+ * order or out of range is skipped (its rows are not written), and query rows
+ * past max_seqlen_q in a longer document are not written. Neither reads or
+ * writes outside the buffers.
+ */
+int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                    int H, int Hkv, int total_q, int total_k, int max_seqlen_q, int d,
+                    float scale, int causal, int window, void* stream);
+
+/*
  * Split-K decode: one query token per sequence against a KV cache
  * ("Quadratic Complexity Bottleneck", KV cache entry: past K and V are read
  * from the cache; "Attention Research", section 2: split-K over keys for
@@ -116,6 +148,22 @@ int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
                        int num_splits, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/*
+ * Split-K decode over caches whose sequences hold different numbers of keys.
+ * Sequence b uses the first kv_lens[b] rows of its [Hkv, Nk, d] cache slot;
+ * its query sits at position kv_lens[b] - 1. Each sequence's own key range is
+ * cut into num_splits chunks of ceil(kv_lens[b] / num_splits) keys, so work
+ * follows the real lengths. kv_lens: DEVICE int32 [B]; values are clamped to
+ * [0, Nk], and a sequence of length 0 gets O = 0, LSE = -inf. Everything else
+ * (layout, workspace size, split count, errors) is as for attn_decode_splitk;
+ * kv_lens must be non-NULL when B > 0.
+ */
+int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_cache,
+                              const int* kv_lens, void* o, float* lse,
+                              int B, int H, int Hkv, int Nk, int d, float scale, int window,
+                              int num_splits, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* The split count attn_decode_splitk uses for these arguments (resolves 0),
  * or a negative status for invalid ones. */
 int attn_decode_num_splits(int B, int Hkv, int Nk, int num_splits);
@@ -134,6 +182,16 @@ int attn_fwd_tile_shape(int d, int is_f32, int* block_m, int* block_n);
 int attn_fwd_tile_counts(const void* q, const void* k, const void* v, void* o, float* lse,
                          int B, int H, int Hkv, int Nq, int Nk, int d,
                          float scale, int causal, int window, int* counts, void* stream);
+
+/* The same for attn_fwd_varlen: counts is device int32
+ * [num_seqs, H, ceil(max_seqlen_q / block_m), 2]; work-groups past their
+ * document's end write (0, 0). Shows that no tile of another document is
+ * ever loaded. */
+int attn_fwd_varlen_tile_counts(const void* q, const void* k, const void* v, void* o,
+                                float* lse, const int* cu_seqlens_q, const int* cu_seqlens_k,
+                                int num_seqs, int H, int Hkv, int total_q, int total_k,
+                                int max_seqlen_q, int d, float scale, int causal, int window,
+                                int* counts, void* stream);
 
 /*
  * Ceiling probes (they compute no attention): the rates this device sustains,

@@ -41,7 +41,8 @@ def test_header_declares_expected_entry_points():
     names = header_functions()
     for n in ["attn_fwd", "attn_fwd_f32", "attn_decode_splitk", "attn_decode_workspace_bytes",
               "attn_strerror", "attn_fwd_tile_shape", "attn_fwd_tile_counts",
-              "attn_decode_num_splits"]:
+              "attn_decode_num_splits", "attn_fwd_varlen", "attn_fwd_varlen_tile_counts",
+              "attn_decode_splitk_varlen"]:
         assert n in names
 
 
@@ -144,6 +145,57 @@ def test_decode_invalid_arguments(lib):
     assert dec(lib, B=0, q=NULL, k=NULL, v=NULL, o=NULL, ws=NULL) == OK
 
 
+def vfwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, cu_q=FAKE, cu_k=FAKE, ns=3, H=4, Hkv=2,
+         tq=40, tk=40, maxq=20, d=128, scale=0.1, causal=1, window=0):
+    return lib.attn_fwd_varlen(q, k, v, o, lse, cu_q, cu_k, ns, H, Hkv, tq, tk, maxq, d,
+                               ctypes.c_float(scale), causal, window, NULL)
+
+
+def test_fwd_varlen_invalid_arguments(lib):
+    assert vfwd(lib, cu_q=NULL) == EINVAL
+    assert vfwd(lib, cu_k=NULL) == EINVAL
+    assert vfwd(lib, q=NULL) == EINVAL
+    assert vfwd(lib, o=NULL) == EINVAL
+    assert vfwd(lib, k=NULL) == EINVAL
+    assert vfwd(lib, ns=-1) == EINVAL
+    assert vfwd(lib, tq=-1) == EINVAL
+    assert vfwd(lib, tk=-1) == EINVAL
+    assert vfwd(lib, maxq=-1) == EINVAL
+    assert vfwd(lib, H=6, Hkv=4) == EINVAL
+    assert vfwd(lib, causal=3) == EINVAL
+    assert vfwd(lib, window=-1) == EINVAL
+    assert vfwd(lib, scale=float("nan")) == EINVAL
+    assert vfwd(lib, d=80) == EUNSUP
+    # nothing to compute: no documents, no query rows, or a zero bound
+    assert vfwd(lib, ns=0, cu_q=NULL, cu_k=NULL) == OK
+    assert vfwd(lib, tq=0, q=NULL, o=NULL, lse=NULL) == OK
+    assert vfwd(lib, maxq=0) == OK
+    st = lib.attn_fwd_varlen_tile_counts(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 3, 4, 2, 40,
+                                         40, 20, 128, ctypes.c_float(0.1), 1, 0, NULL, NULL)
+    assert st == EINVAL
+
+
+def vdec(lib, lens=FAKE, B=2, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, H=8, Hkv=2, Nk=100, d=128, scale=0.1,
+                window=0, splits=4, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    a = args
+    return lib.attn_decode_splitk_varlen(a["q"], a["k"], a["v"], lens, a["o"], a["lse"], B,
+                                         a["H"], a["Hkv"], a["Nk"], a["d"],
+                                         ctypes.c_float(a["scale"]), a["window"], a["splits"],
+                                         a["ws"], a["ws_bytes"], NULL)
+
+
+def test_decode_varlen_invalid_arguments(lib):
+    assert vdec(lib, lens=NULL) == EINVAL
+    assert vdec(lib, q=NULL) == EINVAL
+    assert vdec(lib, H=6, Hkv=4) == EINVAL
+    assert vdec(lib, splits=101) == EINVAL
+    assert vdec(lib, d=32) == EUNSUP
+    assert vdec(lib, ws_bytes=100) == EWS
+    assert vdec(lib, B=0, lens=NULL, q=NULL, k=NULL, v=NULL, o=NULL, ws=NULL) == OK
+
+
 def _no_gpu():
     try:
         import torch
@@ -157,3 +209,5 @@ def test_valid_call_without_device_reports_nodevice(lib):
     # All arguments valid, no HIP device in this process: ENODEVICE, no crash.
     assert fwd(lib) == ENODEV
     assert dec(lib) == ENODEV
+    assert vfwd(lib) == ENODEV
+    assert vdec(lib) == ENODEV

@@ -1,0 +1,308 @@
+"""Packed documents and per-sequence cache lengths: HIP path against the oracle.
+
+Prefill (attn_fwd_varlen): element-wise parity on small packed batches that
+span several tiles with ragged tails, empty documents, documents with more
+or fewer queries than keys, and documents with no keys; exact mask checks
+(q = 0 counts, bit-identical output of the other documents when one is
+changed); per-document tile counts; equal-length documents equal the
+fixed-length kernel bit for bit; the packed workload at full size on
+sampled rows.
+
+Decode (attn_decode_varlen): parity on mixed lengths including 0 and 1;
+cache rows past a sequence's length never matter; full-length sequences
+equal attn_decode bit for bit; each sequence equals a one-query packed
+prefill over its keys; the mixed-length workload at full size, sampled.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import exact_io_aware_06_amd as mi
+from helpers import check_lse, check_out, to64
+from synth import inputs as S
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _gen(seed):
+    return torch.Generator(device="cpu").manual_seed(seed)
+
+
+def packed_case(lq, lk, H, Hkv, d, seed):
+    g = _gen(seed)
+    q = torch.randn(H, sum(lq), d, generator=g).to(torch.bfloat16)
+    k = torch.randn(Hkv, sum(lk), d, generator=g).to(torch.bfloat16)
+    v = torch.randn(Hkv, sum(lk), d, generator=g).to(torch.bfloat16)
+    return q, k, v, S.cu_seqlens(lq), S.cu_seqlens(lk)
+
+
+def run_varlen(q, k, v, cu_q, cu_k, scale, causal, window, max_q=None):
+    lq = np.diff(cu_q)
+    max_q = int(lq.max(initial=0)) if max_q is None else max_q
+    o, lse = mi.attn_fwd_varlen(q.to(DEV), k.to(DEV), v.to(DEV),
+                                torch.from_numpy(cu_q).to(DEV), torch.from_numpy(cu_k).to(DEV),
+                                max_q, scale=scale, causal=causal, window=window)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+DOC_CASES = [
+    # (query lengths, key lengths): self-attention mixes with ragged tails
+    ([300, 1, 129, 64, 700], [300, 1, 129, 64, 700]),
+    ([1000, 0, 77, 256], [1000, 0, 77, 256]),
+    # more keys than queries (a cached prefix), fewer keys than queries
+    # (leading rows empty under causal), a document with queries but no keys
+    ([100, 200, 50, 33], [400, 150, 0, 33]),
+    ([5, 130, 1], [260, 3, 1]),
+]
+
+
+@pytest.mark.parametrize("docs", DOC_CASES)
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal,window", [(1, 0), (0, 0), (1, 100), (0, 64)])
+def test_varlen_parity(docs, d, causal, window):
+    lq, lk = docs
+    H, Hkv = 8, 2
+    q, k, v, cu_q, cu_k = packed_case(lq, lk, H, Hkv, d, seed=len(lq) * 10 + d + causal)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_varlen(q, k, v, cu_q, cu_k, scale, causal, window)
+    o_ref, l_ref = oracle.attention_varlen_ref(q, k, v, cu_q, cu_k, scale, causal, window)
+    label = f"docs={lq}/{lk} d={d} causal={causal} W={window}"
+    check_out(to64(o), o_ref, bf16=True, label=label)
+    check_lse(to64(lse), l_ref, label=label)
+
+
+@pytest.mark.parametrize("docs", DOC_CASES)
+@pytest.mark.parametrize("causal,window", [(1, 0), (1, 37), (0, 0), (0, 5)])
+def test_varlen_zero_queries_count_visible_keys(docs, causal, window):
+    """q = 0: every visible score is 0, so exp(LSE) is the exact visible count."""
+    lq, lk = docs
+    q, k, v, cu_q, cu_k = packed_case(lq, lk, 4, 1, 128, seed=3)
+    q.zero_()
+    _, lse = run_varlen(q, k, v, cu_q, cu_k, 1.0, causal, window)
+    count = oracle.packed_visible_mask(cu_q, cu_k, causal, window).sum(axis=1)
+    lg = to64(lse)
+    for h in range(4):
+        got = np.where(np.isneginf(lg[h]), 0, np.rint(np.exp(lg[h])))
+        assert np.array_equal(got.astype(np.int64), count), f"head {h}"
+
+
+@pytest.mark.parametrize("causal,window", [(1, 0), (0, 0), (1, 50)])
+def test_varlen_no_leakage(causal, window):
+    """Changing one document's K/V leaves every other row bit-identical."""
+    lq = [200, 129, 64, 300]
+    q, k, v, cu_q, cu_k = packed_case(lq, lq, 8, 2, 128, seed=11)
+    o1, l1 = run_varlen(q, k, v, cu_q, cu_k, 0.088, causal, window)
+    e = 1
+    k2, v2 = k.clone(), v.clone()
+    k2[:, cu_k[e]:cu_k[e + 1]] = torch.randn(2, lq[e], 128, generator=_gen(99)).to(torch.bfloat16)
+    v2[:, cu_k[e]:cu_k[e + 1]] = 5.0
+    o2, l2 = run_varlen(q, k2, v2, cu_q, cu_k, 0.088, causal, window)
+    inside = torch.zeros(sum(lq), dtype=torch.bool, device=DEV)
+    inside[cu_q[e]:cu_q[e + 1]] = True
+    assert torch.equal(o1[:, ~inside], o2[:, ~inside])
+    assert torch.equal(l1[:, ~inside], l2[:, ~inside])
+    assert not torch.equal(o1[:, inside], o2[:, inside])
+
+
+@pytest.mark.parametrize("causal,window", [(1, 0), (0, 0), (1, 300)])
+def test_varlen_equal_lengths_match_fixed_kernel(causal, window):
+    """Documents of equal length N are the fixed-length batch, bit for bit."""
+    B, H, Hkv, N, d = 3, 8, 2, 640, 128
+    g = _gen(21)
+    q = torch.randn(B, H, N, d, generator=g).to(torch.bfloat16).to(DEV)
+    k = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16).to(DEV)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16).to(DEV)
+    o_fix, l_fix = mi.attn_fwd(q, k, v, scale=0.088, causal=causal, window=window)
+    pack = lambda x: x.transpose(0, 1).reshape(x.shape[1], B * N, d).contiguous()
+    cu = S.cu_seqlens([N] * B)
+    o, lse = run_varlen(pack(q), pack(k), pack(v), cu, cu, 0.088, causal, window)
+    assert torch.equal(o, pack(o_fix))
+    assert torch.equal(lse, l_fix.transpose(0, 1).reshape(H, B * N))
+
+
+@pytest.mark.parametrize("docs", DOC_CASES)
+@pytest.mark.parametrize("causal,window", [(1, 0), (0, 0), (1, 100), (0, 64)])
+def test_varlen_only_visible_tiles_are_loaded(docs, causal, window):
+    """Per document, exactly the blocks holding a visible pair are loaded;
+    work-groups past a document's end load nothing."""
+    lq, lk = docs
+    H, d = 4, 128
+    q, k, v, cu_q, cu_k = packed_case(lq, lk, H, 2, d, seed=5)
+    max_q = max(lq)
+    o, lse, counts = mi.fwd_varlen_tile_counts(
+        q.to(DEV), k.to(DEV), v.to(DEV), torch.from_numpy(cu_q).to(DEV),
+        torch.from_numpy(cu_k).to(DEV), max_q, scale=0.1, causal=causal, window=window)
+    o2, l2 = run_varlen(q, k, v, cu_q, cu_k, 0.1, causal, window)
+    assert torch.equal(o, o2) and torch.equal(lse, l2)  # instrumentation changes nothing
+    bm, bn = mi.fwd_tile_shape(d)
+    counts = counts.cpu().numpy()
+    nqt = -(-max_q // bm)
+    for e, (nq, nk) in enumerate(zip(lq, lk)):
+        loaded = np.zeros(nqt, dtype=np.int64)
+        masked = np.zeros(nqt, dtype=np.int64)
+        if nq > 0 and nk > 0:
+            need, full = oracle.tiles_needed(nq, nk, causal, window, bm, bn)
+            loaded[:need.shape[0]] = need.sum(axis=1)
+            masked[:need.shape[0]] = (need & ~full).sum(axis=1)
+        for h in range(H):
+            assert np.array_equal(counts[e, h, :, 0], loaded), f"doc {e} head {h}"
+            assert np.array_equal(counts[e, h, :, 1], masked), f"doc {e} head {h}"
+
+
+def test_varlen_bad_offsets_skip_the_document():
+    """Offsets past the packed tensors: that document is skipped, others are right."""
+    lq = [100, 60, 40]
+    q, k, v, cu_q, cu_k = packed_case(lq, lq, 4, 2, 64, seed=8)
+    bad_q, bad_k = cu_q.copy(), cu_k.copy()
+    bad_q[2], bad_k[2] = 10_000, 10_000       # doc 1 ends past the end, doc 2 starts there
+    qd, kd, vd = q.to(DEV), k.to(DEV), v.to(DEV)
+    o = torch.full_like(qd, 7.0)
+    lse = torch.full((4, sum(lq)), 7.0, device=DEV)
+    mi.attn_fwd_varlen(qd, kd, vd, torch.from_numpy(bad_q).to(DEV),
+                       torch.from_numpy(bad_k).to(DEV), 100, scale=0.125, causal=True,
+                       out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen_ref(q, k, v, cu_q, cu_k, 0.125, True, 0)
+    check_out(to64(o[:, :100]), o_ref[:, :100], label="doc 0")
+    check_lse(to64(lse[:, :100]), l_ref[:, :100], label="doc 0")
+    assert torch.all(o[:, 100:] == 7.0) and torch.all(lse[:, 100:] == 7.0)
+
+
+def test_varlen_rows_past_max_seqlen_are_not_written():
+    lq = [300, 100]
+    q, k, v, cu_q, cu_k = packed_case(lq, lq, 2, 1, 128, seed=9)
+    qd = q.to(DEV)
+    o = torch.full_like(qd, 3.0)
+    lse = torch.full((2, 400), 3.0, device=DEV)
+    mi.attn_fwd_varlen(qd, k.to(DEV), v.to(DEV), torch.from_numpy(cu_q).to(DEV),
+                       torch.from_numpy(cu_k).to(DEV), 128, scale=0.09, causal=True,
+                       out=o, lse=lse)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.attention_varlen_ref(q, k, v, cu_q, cu_k, 0.09, True, 0)
+    written = np.r_[0:128, 300:400]
+    check_out(to64(o[:, written]), o_ref[:, written], label="written rows")
+    assert torch.all(o[:, 128:300] == 3.0) and torch.all(lse[:, 128:300] == 3.0)
+
+
+def test_packed_workload_full_size_sampled():
+    """Four 8k contexts packed with log-uniform documents, H32 Hkv8 d128 causal."""
+    cfg = S.PACKED["p1"]
+    lens = cfg.lengths(0)
+    cu = S.cu_seqlens(lens)
+    total = int(cu[-1])
+    q, k, v = S.packed_inputs(cfg, total, total, seed=0, device="cpu")
+    o, lse = run_varlen(q, k, v, cu, cu, cfg.scale, cfg.causal, cfg.window)
+    rng = np.random.default_rng(0)
+    # first and last rows of every document, plus random rows
+    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, rng.integers(0, total, 64)]))
+    og, lg = o.cpu(), lse.cpu()
+    for h in (0, 5, 17, 31):
+        o_ref, l_ref = oracle.attention_varlen_rows_ref(q, k, v, cu, cu, cfg.scale, cfg.causal,
+                                                        cfg.window, h, rows)
+        check_out(to64(og[h, rows]), o_ref, label=f"p1 h{h}")
+        check_lse(to64(lg[h, rows]), l_ref, label=f"p1 h{h}")
+    assert torch.isfinite(lg).all()  # causal self-attention: every row sees itself
+
+
+# --------------------------------------------------------------------------
+# decode with per-sequence cache lengths
+
+
+def run_decode(q, kc, vc, lens, scale, window, splits):
+    o, lse = mi.attn_decode_varlen(q.to(DEV), kc.to(DEV), vc.to(DEV),
+                                   torch.as_tensor(lens, dtype=torch.int32).to(DEV),
+                                   scale=scale, window=window, num_splits=splits)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def decode_case(B, H, Hkv, Nk, d, seed):
+    g = _gen(seed)
+    q = torch.randn(B, H, d, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16)
+    return q, kc, vc
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits,window", [(1, 0), (3, 0), (16, 0), (0, 0), (7, 40)])
+def test_decode_varlen_parity(d, splits, window):
+    lens = [0, 1, 17, 128, 129, 500, 1000]
+    q, kc, vc = decode_case(len(lens), 8, 2, 1000, d, seed=d + splits)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run_decode(q, kc, vc, lens, scale, window, splits)
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, scale, window)
+    label = f"d={d} splits={splits} W={window}"
+    check_out(to64(o), o_ref, label=label)
+    check_lse(to64(lse), l_ref, label=label)
+    assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
+
+
+def test_decode_varlen_ignores_rows_past_length():
+    lens = [3, 700, 1000, 64]
+    q, kc, vc = decode_case(4, 8, 2, 1000, 128, seed=2)
+    o1, l1 = run_decode(q, kc, vc, lens, 0.088, 0, 8)
+    kc2, vc2 = kc.clone(), vc.clone()
+    for b, n in enumerate(lens):
+        kc2[b, :, n:] = 300.0
+        vc2[b, :, n:] = -300.0
+    o2, l2 = run_decode(q, kc2, vc2, lens, 0.088, 0, 8)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+@pytest.mark.parametrize("splits", [1, 5, 16])
+def test_decode_varlen_full_lengths_match_uniform_kernel(splits):
+    q, kc, vc = decode_case(3, 32, 8, 777, 128, seed=4)
+    o1, l1 = run_decode(q, kc, vc, [777] * 3, 0.088, 0, splits)
+    o2, l2 = mi.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), scale=0.088, num_splits=splits)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+
+
+def test_decode_varlen_matches_one_query_packed_prefill():
+    """Sequence b is a one-query document over its kv_lens[b] keys."""
+    lens = [1, 90, 300, 129]
+    B, H, Hkv, Nk, d = len(lens), 8, 2, 300, 128
+    q, kc, vc = decode_case(B, H, Hkv, Nk, d, seed=6)
+    o_dec, l_dec = run_decode(q, kc, vc, lens, 0.088, 0, 4)
+    qp = q.transpose(0, 1).contiguous()                      # [H, B, d]: one row per document
+    kp = torch.cat([kc[b, :, :n] for b, n in enumerate(lens)], dim=1).contiguous()
+    vp = torch.cat([vc[b, :, :n] for b, n in enumerate(lens)], dim=1).contiguous()
+    o_pre, l_pre = run_varlen(qp, kp, vp, S.cu_seqlens([1] * B), S.cu_seqlens(lens), 0.088,
+                              True, 0)
+    ref_o, ref_l = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.088, 0)
+    check_out(to64(o_dec), ref_o, label="decode")
+    check_out(to64(o_pre.transpose(0, 1)), ref_o, label="packed prefill")
+    assert float((o_dec.float() - o_pre.transpose(0, 1).float()).abs().max()) <= 2e-2
+    check_lse(to64(l_pre.transpose(0, 1)), ref_l, label="packed prefill lse")
+
+
+def test_decode_kvlens_workload_full_size_sampled():
+    """B=64, H32 Hkv8, 32k-key cache slots, lengths uniform in [1, 32768], 16 splits."""
+    c = S.DECODE_KVLENS
+    lens = S.kv_lengths(0, c.B, c.Nk)
+    q, kc, vc = S.decode_inputs(c, 0, device=DEV)
+    o, lse = mi.attn_decode_varlen(q, kc, vc, torch.from_numpy(lens).to(DEV), scale=c.scale,
+                                   num_splits=c.splits)
+    torch.cuda.synchronize()
+    og, lg = o.cpu(), lse.cpu()
+    for b in (0, 7, int(np.argmin(lens)), int(np.argmax(lens)), 63):
+        o_ref, l_ref = _decode_rows(q, kc, vc, lens, c, b)
+        check_out(to64(og[b]), o_ref, label=f"k1 b{b}")
+        check_lse(to64(lg[b]), l_ref, label=f"k1 b{b}")
+    del kc, vc
+
+
+def _decode_rows(q, kc, vc, lens, c, b):
+    """Oracle for sequence b, reading only its first kv_lens[b] cache rows."""
+    n = int(lens[b])
+    qb = q[b:b + 1].cpu()
+    kb, vb = kc[b:b + 1, :, :n].cpu(), vc[b:b + 1, :, :n].cpu()
+    return oracle.decode_kvlens_rows_ref(qb, kb, vb, [n], c.scale, c.window, 0, list(range(c.H)))
