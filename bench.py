@@ -10,7 +10,13 @@ LSE) is reported beside it. Kernel durations come from HIP events recorded on
 the stream the kernels are launched on, around each call inside the timed
 steps.
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+Beside the step, and timed in a loop of their own over the same number of
+steps, two variants are measured: packed-document prefill (four 8k contexts
+filled with documents of log-uniform length, the mask restarting at every
+document) and the decode over the same cache buffers with a random length
+per sequence.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extensions]
 """
 
 from __future__ import annotations
@@ -127,6 +133,41 @@ def measure_ceilings(torch, mi, dev):
                       "best of 3"}
 
 
+SWEEP_N = [1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072]
+
+
+def context_sweep(torch, synth, mi, accounting, dev, steps, warmup):
+    """Causal GQA prefill (B1 H32 Hkv8 d128, scale 1/sqrt(d)) over context lengths."""
+    base = synth.CONFIGS["c4"].with_(window=0)
+    rows = []
+    for n in SWEEP_N:
+        c = base.with_(name=f"causal{n}", Nq=n, Nk=n)
+        q, k, v = synth.prefill_inputs(c, 0, device=dev)
+        o = torch.empty_like(q)
+        lse = torch.empty(c.B, c.H, c.Nq, dtype=torch.float32, device=dev)
+        call = lambda: mi.attn_fwd(q, k, v, scale=c.scale, causal=1, out=o, lse=lse)
+        for _ in range(warmup):
+            call()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record()
+            call()
+            b.record()
+        torch.cuda.synchronize()
+        ms = sorted(a.elapsed_time(b) for a, b in evs)
+        flops = accounting.prefill_flops(c.B, c.H, n, n, c.d, 1, 0)
+        med = ms[len(ms) // 2]
+        tf = flops / (med * 1e-3) / 1e12
+        rows.append({"N": n, "ms_median": round(med, 4), "ms_min": round(ms[0], 4),
+                     "tflops": round(tf, 1), "frac_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+                     "algorithmic_flops": flops})
+        print(f"sweep N={n}: {med:.4f} ms, {tf:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del q, k, v, o, lse
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,8 +176,12 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32"], default="all",
-                    help="launch only one part of the step (for profiling runs)")
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens"],
+                    default="all", help="launch only one part (for profiling runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
+    ap.add_argument("--no-extensions", action="store_true",
+                    help="skip the packed-document prefill and mixed-length decode legs")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the measured matrix-core / read-bandwidth ceilings")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
@@ -161,6 +206,12 @@ def main():
         build.build()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.sweep:
+        rows = context_sweep(torch, synth, mi, accounting, dev, max(3, min(args.steps, 20)),
+                             max(1, min(args.warmup, 3)))
+        print(json.dumps({"sweep": "causal GQA prefill B1 H32 Hkv8 d128 bf16, scale 1/sqrt(d), "
+                                   "N(0,1) inputs", "unit": "TFLOP/s", "points": rows}))
+        return
 
     cp = synth.CONFIGS["c3"]
     cd = synth.CONFIGS["c5"]
@@ -177,28 +228,38 @@ def main():
     of = torch.empty_like(qf)
     lsef = torch.empty(cf.B, cf.H, cf.Nq, dtype=torch.float32, device=dev)
 
-    run_pre = args.only in ("all", "prefill")
-    run_dec = args.only in ("all", "decode")
-    run_f32 = args.only in ("all", "fp32")
+    # Packed documents (four 8k contexts of log-uniform documents) and decode
+    # over the same cache buffers with per-sequence lengths.
+    cpk = synth.inputs.PACKED["p1"]
+    pk_lens = cpk.lengths(0)
+    pk_cu = synth.inputs.cu_seqlens(pk_lens)
+    pk_total = int(pk_cu[-1])
+    qp, kp, vp = synth.inputs.packed_inputs(cpk, pk_total, pk_total, seed=0, device=dev)
+    cu_dev = torch.from_numpy(pk_cu).to(dev)
+    op = torch.empty_like(qp)
+    lsep = torch.empty(cpk.H, pk_total, dtype=torch.float32, device=dev)
+    ck = synth.inputs.DECODE_KVLENS
+    kv_lens = synth.inputs.kv_lengths(0, ck.B, ck.Nk)
+    kv_lens_dev = torch.from_numpy(kv_lens).to(dev)
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        if run_pre:
-            mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal, window=cp.window, out=o,
-                        lse=lse)
-        if ev is not None:
-            ev[1].record()
-        if run_dec:
-            mi.attn_decode(qd, kc, vc, scale=cd.scale, window=cd.window, num_splits=cd.splits,
-                           out=od, lse=lsed, workspace=ws)
-        if ev is not None:
-            ev[2].record()
-        if run_f32:
-            mi.attn_fwd(qf, kf, vf, scale=cf.scale, causal=cf.causal, window=cf.window, out=of,
-                        lse=lsef)
-        if ev is not None:
-            ev[3].record()
+    parts = {
+        "prefill": lambda: mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal,
+                                       window=cp.window, out=o, lse=lse),
+        "decode": lambda: mi.attn_decode(qd, kc, vc, scale=cd.scale, window=cd.window,
+                                         num_splits=cd.splits, out=od, lse=lsed, workspace=ws),
+        "fp32": lambda: mi.attn_fwd(qf, kf, vf, scale=cf.scale, causal=cf.causal,
+                                    window=cf.window, out=of, lse=lsef),
+        "packed": lambda: mi.attn_fwd_varlen(qp, kp, vp, cu_dev, cu_dev, max(pk_lens),
+                                             scale=cpk.scale, causal=cpk.causal,
+                                             window=cpk.window, out=op, lse=lsep),
+        "kvlens": lambda: mi.attn_decode_varlen(qd, kc, vc, kv_lens_dev, scale=ck.scale,
+                                                window=ck.window, num_splits=ck.splits,
+                                                out=od, lse=lsed, workspace=ws),
+    }
+    core = ["prefill", "decode", "fp32"]
+    ext = [] if args.no_extensions else ["packed", "kvlens"]
+    if args.only != "all":
+        core, ext = [args.only], []
 
     if args.calib_copy > 0:
         nbytes = args.calib_copy << 20
@@ -210,19 +271,32 @@ def main():
         print(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written", file=sys.stderr)
         del src, dst
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(events[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
-    f32_ms = [e[2].elapsed_time(e[3]) for e in events]
+    def timed(names):
+        """Warm up, then time `args.steps` passes over `names`; per-part event times."""
+        for _ in range(args.warmup):
+            for n in names:
+                parts[n]()
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            evs[i][0].record()
+            for j, n in enumerate(names):
+                parts[n]()
+                evs[i][j + 1].record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ms = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
+        return wall, ms
+
+    wall, ms = timed(core)
+    ext_ms = timed(ext)[1] if ext else {}
+    ms.update(ext_ms)
+    pre_ms = ms.get("prefill", [0.0])
+    dec_ms = ms.get("decode", [0.0])
+    f32_ms = ms.get("fp32", [0.0])
     mean = lambda xs: sum(xs) / len(xs)
 
     pre_flops = accounting.prefill_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
@@ -232,12 +306,17 @@ def main():
     ceilings = None if args.no_ceilings else measure_ceilings(torch, mi, dev)
     pre_tflops = rate(pre_flops, mean(pre_ms)) / 1e12
     dec_gbs = rate(dec_bytes, mean(dec_ms)) / 1e9
+    pk_flops = accounting.packed_flops(cpk.H, pk_cu, pk_cu, cpk.d, cpk.causal, cpk.window)
+    kvl_bytes = accounting.decode_kvlens_bytes(ck.H, ck.Hkv, kv_lens, ck.d, window=ck.window)
     if args.only != "all":
-        part = {"prefill": (pre_ms, pre_tflops, "TFLOP/s"), "decode": (dec_ms, dec_gbs, "GB/s"),
-                "fp32": (f32_ms, rate(f32_flops, mean(f32_ms)) / 1e12, "TFLOP/s")}[args.only]
-        print(json.dumps({"only": args.only, "ms": round(mean(part[0]), 4),
-                          "ms_min": round(min(part[0]), 4), "value": round(part[1], 2),
-                          "unit": part[2], "steps": args.steps}))
+        xs = ms[args.only]
+        val, unit = {"prefill": (pre_tflops, "TFLOP/s"), "decode": (dec_gbs, "GB/s"),
+                     "fp32": (rate(f32_flops, mean(f32_ms)) / 1e12, "TFLOP/s"),
+                     "packed": (rate(pk_flops, mean(xs)) / 1e12, "TFLOP/s"),
+                     "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s")}[args.only]
+        print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
+                          "ms_min": round(min(xs), 4), "value": round(val, 2),
+                          "unit": unit, "steps": args.steps}))
         return
 
     out = {
@@ -280,6 +359,25 @@ def main():
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_for("decode")},
     }
+    if "packed" in ms:
+        pk_tf = rate(pk_flops, mean(ms["packed"])) / 1e12
+        out["packed_prefill"] = {
+            "workload": f"packed causal GQA prefill: {len(pk_lens)} documents (log-uniform "
+                        f"{cpk.min_len}..{cpk.max_len}) in {cpk.contexts} x {cpk.context_len} "
+                        f"tokens, H{cpk.H} Hkv{cpk.Hkv} d{cpk.d} bf16",
+            "documents": len(pk_lens), "tokens": pk_total, "algorithmic_flops": pk_flops,
+            "ms": round(mean(ms["packed"]), 4), "ms_min": round(min(ms["packed"]), 4),
+            "value": round(pk_tf, 2), "unit": "TFLOP/s",
+            "frac_peak": round(pk_tf / PEAK_BF16_TFLOPS, 4)}
+    if "kvlens" in ms:
+        kv_gbs = rate(kvl_bytes, mean(ms["kvlens"])) / 1e9
+        out["decode_kvlens"] = {
+            "workload": f"split-K decode B{ck.B} H{ck.H} Hkv{ck.Hkv} d{ck.d}, cache slots of "
+                        f"{ck.Nk} keys holding uniform random lengths in [1, {ck.Nk}] "
+                        f"(total {int(kv_lens.sum())} keys), {ck.splits} splits",
+            "algorithmic_bytes": kvl_bytes,
+            "ms": round(mean(ms["kvlens"]), 4), "ms_min": round(min(ms["kvlens"]), 4),
+            "value": round(kv_gbs, 1), "unit": "GB/s", "frac_hbm": round(kv_gbs / PEAK_HBM_GBS, 4)}
     if ceilings:
         out["roofline"]["frac_of_measured_ceiling"] = round(
             pre_tflops / ceilings["mfma_bf16_tflops"], 4)

@@ -162,6 +162,19 @@ def test_workload_sliding_window(seed):
     check_sampled(c, q, k, v, o, lse, heads, lambda r: sample_rows(c.Nq, r, extra), seed)
 
 
+@pytest.mark.parametrize("N", [65536, 131072])
+def test_long_context_sampled(N):
+    """The context sweep's longest points: causal GQA, B1 H32 Hkv8 d128, on
+    sampled rows (each oracle row spans all N keys)."""
+    c = synth.CONFIGS["c4"].with_(name=f"causal{N}", Nq=N, Nk=N, window=0)
+    q, k, v = synth.prefill_inputs(c, 0, device=DEV)
+    o, lse = mi.attn_fwd(q, k, v, scale=c.scale, causal=c.causal, window=c.window)
+    torch.cuda.synchronize()
+    heads = [0, 17, 31]
+    check_sampled(c, q, k, v, o, lse, heads,
+                  lambda r: sample_rows(c.Nq, r, (N // 4, 3 * N // 4)), 0)
+
+
 def test_repeated_runs_bit_identical():
     c = synth.CONFIGS["c3"].with_(H=8, Hkv=2, Nq=2048, Nk=2048)
     q, k, v = synth.prefill_inputs(c, 5)
