@@ -21,8 +21,8 @@ Modules:
   online     - the pages' online-softmax recurrence and the split-K merge, as
                independent fp64 models used only to pin the definition
   tiles      - which (query-tile, key-tile) blocks hold any visible pair
-  varlen     - packed documents (block-diagonal mask) and decode over caches
-               of per-sequence length
+  varlen     - packed documents (block-diagonal mask), decode over caches
+               of per-sequence length and over paged caches
 """
 
 from .attention import (  # noqa: F401
@@ -41,4 +41,6 @@ from .varlen import (  # noqa: F401
     attention_varlen_rows_ref,
     decode_kvlens_ref,
     decode_kvlens_rows_ref,
+    decode_paged_ref,
+    gather_pages,
 )

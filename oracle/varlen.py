@@ -23,6 +23,11 @@ Readings (the pages give no layout or interface for packing):
     valid keys at the front of a [B, Hkv, Nk, d] buffer; its query sits at
     position kv_lens[b] - 1, and keys past kv_lens[b] do not exist for it.
     A sequence with no key gets O = 0, LSE = -inf.
+  * paged KV cache ("Attention Research", section 2, which lists paged
+    variants among attention kernel libraries; the KV cache itself is in
+    "Quadratic Complexity Bottleneck"): pools of fixed-size pages
+    [num_pages, Hkv, page_size, d] and a block table naming, for each
+    sequence, the physical page of its j-th run of page_size keys.
 """
 
 from __future__ import annotations
@@ -171,3 +176,49 @@ def decode_kvlens_rows_ref(q, k_cache, v_cache, kv_lens, scale: float, window: i
         out_o.append(od[0])
         out_l.append(ld[0])
     return np.stack(out_o), np.array(out_l)
+
+
+def gather_pages(pages, block_table, b: int, n: int, page_size: int) -> np.ndarray:
+    """Sequence b's first n cache rows [Hkv, n, d] from a page pool [P, Hkv, page_size, d].
+
+    Key j of sequence b lives in physical page block_table[b][j // page_size],
+    row j % page_size.
+    """
+    rows = []
+    for j in range(0, n, page_size):
+        pg = int(block_table[b][j // page_size])
+        take = min(page_size, n - j)
+        rows.append(_f64(pages[pg][:, :take]))
+    if not rows:
+        return np.zeros((pages.shape[1], 0, pages.shape[3]))
+    return np.concatenate(rows, axis=1)
+
+
+def decode_paged_ref(q, k_pages, v_pages, block_table, kv_lens, page_size: int, scale: float,
+                     window: int = 0, seqs=None, heads=None):
+    """Decode over a paged KV cache: (O [len(seqs), len(heads), d], LSE) in float64.
+
+    Reading (the pages name paged KV caches without a layout): K and V pages
+    form pools [num_pages, Hkv, page_size, d]; sequence b holds kv_lens[b]
+    keys whose j-th page is block_table[b][j]. Each sequence is gathered into
+    a contiguous cache and attended as in decode_kvlens_ref.
+    """
+    q64 = _f64(q)
+    B, H, d = q64.shape
+    Hkv = k_pages.shape[1]
+    G = H // Hkv
+    seqs = range(B) if seqs is None else list(seqs)
+    heads = range(H) if heads is None else list(heads)
+    o = np.zeros((len(seqs), len(heads), d))
+    lse = np.full((len(seqs), len(heads)), -np.inf)
+    for si, b in enumerate(seqs):
+        n = int(kv_lens[b])
+        if n <= 0:
+            continue
+        kb = gather_pages(k_pages, block_table, b, n, page_size)
+        vb = gather_pages(v_pages, block_table, b, n, page_size)
+        vis = visible_mask(1, n, True, window)
+        for hi, h in enumerate(heads):
+            od, ld, _ = _head_rows(q64[b, h:h + 1], kb[h // G], vb[h // G], float(scale), vis)
+            o[si, hi], lse[si, hi] = od[0], ld[0]
+    return o, lse

@@ -243,3 +243,38 @@ def packed_inputs(cfg: PackedConfig, total_q: int, total_k: int, seed: int, devi
     k = gen_normal((cfg.Hkv, total_k, cfg.d), seed, TID_K, 0, cfg.dtype, 1.0, device)
     v = gen_normal((cfg.Hkv, total_k, cfg.d), seed, TID_V, 0, cfg.dtype, 1.0, device)
     return q, k, v
+
+
+def paged_block_table(seed: int, kv_lens, page_size: int, max_pages: int | None = None):
+    """(block_table int32 [B, max_pages], num_pages) for a fragmented page pool.
+
+    Sequence b gets ceil(kv_lens[b] / page_size) pages. The physical page ids
+    are a seeded random permutation of 0 .. num_pages - 1, so neighbouring
+    pages of a sequence are scattered over the pool; unused entries are -1.
+    """
+    lens = np.asarray(kv_lens, dtype=np.int64)
+    need = -(-lens // page_size)
+    num_pages = int(need.sum())
+    width = int(need.max(initial=0)) if max_pages is None else int(max_pages)
+    rng = np.random.default_rng(seed_key(seed, TID_LEN, 1))
+    perm = rng.permutation(num_pages)
+    table = np.full((lens.size, max(width, 1)), -1, dtype=np.int32)
+    at = 0
+    for b, n in enumerate(need):
+        table[b, :n] = perm[at:at + n]
+        at += n
+    return table, num_pages
+
+
+# Paged decode: the mixed-length decode workload stored in 16-key pages
+# scattered over one pool.
+PAGED = {"page_size": 16, "decode": CONFIGS["c5"].with_(name="g1",
+                                                         note="split-K decode over a paged cache")}
+
+
+def paged_inputs(cfg: DecodeConfig, num_pages: int, page_size: int, seed: int, device="cpu"):
+    """(q [B,H,d], k_pages, v_pages [num_pages, Hkv, page_size, d]) for paged decode."""
+    q = gen_normal((cfg.B, cfg.H, cfg.d), seed, TID_Q, 0, cfg.dtype, 1.0, device)
+    k = gen_normal((num_pages, cfg.Hkv, page_size, cfg.d), seed, TID_K, 0, cfg.dtype, 1.0, device)
+    v = gen_normal((num_pages, cfg.Hkv, page_size, cfg.d), seed, TID_V, 0, cfg.dtype, 1.0, device)
+    return q, k, v

@@ -13,7 +13,11 @@ itself:
   pinned against torch and brute force), only laid out differently;
 * decode: rows past a sequence's length never matter; a full-length
   sequence is plain decode; an empty one is O = 0, LSE = -inf;
-* closed form: with q = 0 every visible score is 0, so LSE = ln(count).
+* closed form: with q = 0 every visible score is 0, so LSE = ln(count);
+* paged caches: scalar loops that address key j as (page j // page_size,
+  row j % page_size); in-order pages equal the contiguous cache; moving pages
+  physically (and the table with them) changes nothing; sequences naming the
+  same physical pages share those keys.
 """
 
 import math
@@ -285,3 +289,99 @@ def test_kv_lengths_range():
     lens = S.kv_lengths(0, 64, 32768)
     assert lens.dtype == np.int32 and lens.min() >= 1 and lens.max() <= 32768
     assert np.array_equal(lens, S.kv_lengths(0, 64, 32768))
+
+
+# --------------------------------------------------------------------------
+# decode over a paged cache
+
+
+def brute_paged(q, kp, vp, table, lens, ps, scale, window):
+    B, H, d = q.shape
+    G = H // kp.shape[1]
+    O = np.zeros((B, H, vp.shape[3]))
+    L = np.full((B, H), -math.inf)
+    for b in range(B):
+        n = int(lens[b])
+        keys = list(range(max(0, n - 1 - window) if window else 0, n))
+        for h in range(H):
+            if not keys:
+                continue
+            g = h // G
+            addr = [(int(table[b][j // ps]), j % ps) for j in keys]
+            sc = [scale * math.fsum(q[b, h, c] * kp[pg, g, r, c] for c in range(d)) for pg, r in addr]
+            mx = max(sc)
+            w = [math.exp(s - mx) for s in sc]
+            den = math.fsum(w)
+            for c in range(vp.shape[3]):
+                O[b, h, c] = math.fsum(w[t] * vp[pg, g, r, c] for t, (pg, r) in enumerate(addr)) / den
+            L[b, h] = mx + math.log(den)
+    return O, L
+
+
+@pytest.mark.parametrize("ps", [2, 4])
+@pytest.mark.parametrize("window", [0, 3])
+def test_paged_brute_force(ps, window):
+    lens = np.array([7, 0, 1, 8, 5])
+    table, npg = S.paged_block_table(3, lens, ps)
+    H, Hkv, d = 4, 2, 3
+    q = RNG.standard_normal((len(lens), H, d))
+    kp = RNG.standard_normal((npg, Hkv, ps, d))
+    vp = RNG.standard_normal((npg, Hkv, ps, d))
+    o, lse = oracle.decode_paged_ref(q, kp, vp, table, lens, ps, 0.7, window)
+    bo, bl = brute_paged(q, kp, vp, table, lens, ps, 0.7, window)
+    assert np.array_equal(np.isinf(lse), np.isinf(bl))
+    fin = np.isfinite(bl)
+    assert np.max(np.abs(lse[fin] - bl[fin])) < 1e-12
+    assert np.max(np.abs(o - bo)) < 1e-12
+
+
+def test_paged_in_order_pages_equal_contiguous_cache():
+    B, H, Hkv, Nk, d, ps = 3, 4, 2, 12, 5, 4
+    q = RNG.standard_normal((B, H, d))
+    kc = RNG.standard_normal((B, Hkv, Nk, d))
+    vc = RNG.standard_normal((B, Hkv, Nk, d))
+    lens = np.array([12, 5, 9])
+    mp = Nk // ps
+    to_pages = lambda c: c.reshape(B, Hkv, mp, ps, d).transpose(0, 2, 1, 3, 4).reshape(B * mp, Hkv, ps, d)
+    table = np.arange(B * mp).reshape(B, mp)
+    o, lse = oracle.decode_paged_ref(q, to_pages(kc), to_pages(vc), table, lens, ps, 0.4, 0)
+    ro, rl = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.4, 0)
+    assert np.max(np.abs(o - ro)) < 1e-14 and np.max(np.abs(lse - rl)) < 1e-14
+
+
+def test_paged_physical_permutation_is_invisible():
+    lens = np.array([9, 14, 3])
+    ps = 4
+    table, npg = S.paged_block_table(0, lens, ps)
+    q = RNG.standard_normal((3, 4, 6))
+    kp = RNG.standard_normal((npg, 1, ps, 6))
+    vp = RNG.standard_normal((npg, 1, ps, 6))
+    o, lse = oracle.decode_paged_ref(q, kp, vp, table, lens, ps, 0.5, 0)
+    perm = RNG.permutation(npg)          # physical page p moves to slot perm[p]
+    kp2, vp2 = np.empty_like(kp), np.empty_like(vp)
+    kp2[perm], vp2[perm] = kp, vp
+    table2 = np.where(table >= 0, perm[np.maximum(table, 0)], -1)
+    o2, lse2 = oracle.decode_paged_ref(q, kp2, vp2, table2, lens, ps, 0.5, 0)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+def test_paged_shared_prefix_pages():
+    """Two sequences naming the same physical pages see the same keys."""
+    ps = 4
+    kp = RNG.standard_normal((5, 1, ps, 3))
+    vp = RNG.standard_normal((5, 1, ps, 3))
+    q = np.repeat(RNG.standard_normal((1, 2, 3)), 2, axis=0)
+    table = np.array([[0, 1, 2], [0, 1, 4]])
+    o, lse = oracle.decode_paged_ref(q, kp, vp, table, [10, 8], ps, 0.5, 0)
+    ro, rl = oracle.decode_paged_ref(q[:1], kp, vp, table[:1], [8], ps, 0.5, 0)
+    assert np.array_equal(o[1], ro[0]) and np.array_equal(lse[1], rl[0])
+
+
+def test_paged_block_table_generator():
+    lens = S.kv_lengths(0, 64, 32768)
+    table, npg = S.paged_block_table(0, lens, 16)
+    need = -(-lens.astype(np.int64) // 16)
+    assert npg == need.sum() and table.shape == (64, need.max())
+    used = np.concatenate([table[b, :need[b]] for b in range(64)])
+    assert np.array_equal(np.sort(used), np.arange(npg))          # each page once
+    assert all(np.all(table[b, need[b]:] == -1) for b in range(64))
