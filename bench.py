@@ -11,10 +11,11 @@ the stream the kernels are launched on, around each call inside the timed
 steps.
 
 Beside the step, and timed in a loop of their own over the same number of
-steps, two variants are measured: packed-document prefill (four 8k contexts
-filled with documents of log-uniform length, the mask restarting at every
-document) and the decode over the same cache buffers with a random length
-per sequence.
+steps, three variants are measured: packed-document prefill (four 8k
+contexts filled with documents of log-uniform length, the mask restarting at
+every document), the decode over the same cache buffers with a random length
+per sequence, and that decode with its keys in 16-key pages scattered over
+one pool.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extensions]
 """
@@ -176,7 +177,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens"],
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens",
+                                       "paged"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
@@ -241,6 +243,12 @@ def main():
     ck = synth.inputs.DECODE_KVLENS
     kv_lens = synth.inputs.kv_lengths(0, ck.B, ck.Nk)
     kv_lens_dev = torch.from_numpy(kv_lens).to(dev)
+    # The same lengths stored in 16-key pages scattered over one pool.
+    cg = synth.inputs.PAGED["decode"]
+    page_size = synth.inputs.PAGED["page_size"]
+    pg_table, num_pages = synth.inputs.paged_block_table(0, kv_lens, page_size)
+    qg, kpg, vpg = synth.inputs.paged_inputs(cg, num_pages, page_size, seed=0, device=dev)
+    pg_table_dev = torch.from_numpy(pg_table).to(dev)
 
     parts = {
         "prefill": lambda: mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal,
@@ -255,9 +263,13 @@ def main():
         "kvlens": lambda: mi.attn_decode_varlen(qd, kc, vc, kv_lens_dev, scale=ck.scale,
                                                 window=ck.window, num_splits=ck.splits,
                                                 out=od, lse=lsed, workspace=ws),
+        "paged": lambda: mi.attn_decode_paged(qg, kpg, vpg, pg_table_dev, kv_lens_dev,
+                                              scale=cg.scale, window=cg.window,
+                                              num_splits=cg.splits, out=od, lse=lsed,
+                                              workspace=ws),
     }
     core = ["prefill", "decode", "fp32"]
-    ext = [] if args.no_extensions else ["packed", "kvlens"]
+    ext = [] if args.no_extensions else ["packed", "kvlens", "paged"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -308,12 +320,15 @@ def main():
     dec_gbs = rate(dec_bytes, mean(dec_ms)) / 1e9
     pk_flops = accounting.packed_flops(cpk.H, pk_cu, pk_cu, cpk.d, cpk.causal, cpk.window)
     kvl_bytes = accounting.decode_kvlens_bytes(ck.H, ck.Hkv, kv_lens, ck.d, window=ck.window)
+    pg_bytes = accounting.decode_paged_bytes(cg.H, cg.Hkv, kv_lens, cg.d, page_size,
+                                             window=cg.window)
     if args.only != "all":
         xs = ms[args.only]
         val, unit = {"prefill": (pre_tflops, "TFLOP/s"), "decode": (dec_gbs, "GB/s"),
                      "fp32": (rate(f32_flops, mean(f32_ms)) / 1e12, "TFLOP/s"),
                      "packed": (rate(pk_flops, mean(xs)) / 1e12, "TFLOP/s"),
-                     "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s")}[args.only]
+                     "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s"),
+                     "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s")}[args.only]
         print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
                           "ms_min": round(min(xs), 4), "value": round(val, 2),
                           "unit": unit, "steps": args.steps}))
@@ -378,6 +393,14 @@ def main():
             "algorithmic_bytes": kvl_bytes,
             "ms": round(mean(ms["kvlens"]), 4), "ms_min": round(min(ms["kvlens"]), 4),
             "value": round(kv_gbs, 1), "unit": "GB/s", "frac_hbm": round(kv_gbs / PEAK_HBM_GBS, 4)}
+    if "paged" in ms:
+        pg_gbs = rate(pg_bytes, mean(ms["paged"])) / 1e9
+        out["decode_paged"] = {
+            "workload": f"the mixed-length decode with its keys in {page_size}-key pages "
+                        f"scattered over one pool of {num_pages} pages",
+            "algorithmic_bytes": pg_bytes,
+            "ms": round(mean(ms["paged"]), 4), "ms_min": round(min(ms["paged"]), 4),
+            "value": round(pg_gbs, 1), "unit": "GB/s", "frac_hbm": round(pg_gbs / PEAK_HBM_GBS, 4)}
     if ceilings:
         out["roofline"]["frac_of_measured_ceiling"] = round(
             pre_tflops / ceilings["mfma_bf16_tflops"], 4)

@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     attn_fwd_varlen,
     attn_decode,
     attn_decode_varlen,
+    attn_decode_paged,
     decode_workspace_bytes,
     fwd_tile_counts,
     fwd_varlen_tile_counts,

@@ -108,3 +108,10 @@ def decode_kvlens_bytes(H, Hkv, kv_lens, d, elem_bytes=2, window=0, lse=True) ->
     kv = 2 * Hkv * keys * d * elem_bytes
     qo = 2 * B * H * d * elem_bytes
     return kv + qo + (B * H * 4 if lse else 0)
+
+
+def decode_paged_bytes(H, Hkv, kv_lens, d, page_size, elem_bytes=2, window=0, lse=True) -> int:
+    """Compulsory bytes of one paged decode step: the keys and values each
+    sequence sees, q, O and LSE, plus the block-table entries of its pages."""
+    pages = sum(-(-int(n) // page_size) for n in kv_lens)
+    return decode_kvlens_bytes(H, Hkv, kv_lens, d, elem_bytes, window, lse) + 4 * pages

@@ -59,6 +59,9 @@ def load_library():
         lib.attn_decode_splitk_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P,
                                                   S, P]
         lib.attn_decode_splitk_varlen.restype = I
+        lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P,
+                                          S, P]
+        lib.attn_decode_paged.restype = I
         lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
         lib.attn_fwd_tile_shape.restype = I
         lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -311,6 +314,52 @@ def attn_decode_varlen(q, k_cache, v_cache, kv_lens, scale=None, window=0, num_s
                                              int(num_splits), _ptr(workspace),
                                              ctypes.c_size_t(workspace.numel()),
                                              _stream(q.device)))
+    return out, lse
+
+
+def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale=None, window=0,
+                      num_splits=0, out=None, lse=None, workspace=None):
+    """Split-K decode over a paged cache.
+
+    q [B,H,d] bf16; k_pages/v_pages [num_pages, Hkv, page_size, d] bf16;
+    block_table int32 [B, max_pages] and kv_lens int32 [B], both on q's GPU.
+    Returns (O [B,H,d] bf16, LSE [B,H] fp32).
+    """
+    import torch
+    _require(q.dim() == 3 and k_pages.dim() == 4 and v_pages.shape == k_pages.shape,
+             "q [B,H,d], pages [num_pages, Hkv, page_size, d]")
+    _require(q.is_cuda and k_pages.device == q.device and v_pages.device == q.device,
+             "tensors must be on the same GPU")
+    _require(q.dtype == torch.bfloat16 and k_pages.dtype == torch.bfloat16
+             and v_pages.dtype == torch.bfloat16, "decode takes bfloat16")
+    _require(q.is_contiguous() and k_pages.is_contiguous() and v_pages.is_contiguous(),
+             "tensors must be contiguous")
+    B, H, d = q.shape
+    num_pages, Hkv, page_size = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    _require(k_pages.shape[3] == d, "head dim mismatch")
+    _require(block_table.dim() == 2 and block_table.shape[0] == B
+             and block_table.dtype == torch.int32 and block_table.device == q.device
+             and block_table.is_contiguous(), "block_table must be contiguous int32 [B, max_pages]")
+    _require(kv_lens.shape == (B,) and kv_lens.dtype == torch.int32
+             and kv_lens.device == q.device and kv_lens.is_contiguous(),
+             "kv_lens must be contiguous int32 [B] on q's GPU")
+    max_pages = block_table.shape[1]
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    nbytes = int(lib.attn_decode_workspace_bytes(B, H, Hkv, max_pages * page_size, d,
+                                                 int(num_splits)))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
+                                     _ptr(kv_lens), _ptr(out), _ptr(lse), B, H, Hkv, d,
+                                     page_size, num_pages, max_pages, ctypes.c_float(scale),
+                                     int(window), int(num_splits), _ptr(workspace),
+                                     ctypes.c_size_t(workspace.numel()), _stream(q.device)))
     return out, lse
 
 

@@ -9,6 +9,11 @@
 // chunks, and each (sequence, KV head, chunk) becomes one work-group that
 // reads its K/V rows exactly once for all G query heads sharing that KV head.
 //
+// A paged cache changes only where a key row is read from: row j of a
+// sequence lives in page block_table[b][j / page_size] of a page pool, at row
+// j % page_size ("Attention Research", section 2, names paged variants of the
+// attention kernels).
+//
 // Split kernel: the work-group walks its chunk in tiles of 128 keys staged
 // through LDS (K as rows, V transposed, as in the prefill kernel); wave w
 // takes keys [32w, 32w + 32) of each tile and treats the G query heads as the
@@ -44,6 +49,12 @@ struct SplitParams {
   int window;
   float scale, scale_log2, thr_raw;
   const int* kv_lens;  // per-sequence key counts, or null (all Nk)
+  // Paged cache: k, v are page pools [num_pages, Hkv, page_size, d] and
+  // block_table [B, max_pages] names the physical page of each sequence's
+  // j-th run of page_size keys (Nk = max_pages * page_size).
+  const int* block_table;
+  int page_shift;  // log2(page_size)
+  int max_pages, num_pages;
 };
 
 struct MergeParams {
@@ -69,10 +80,13 @@ struct DTile {
   static_assert((4 * 32 * D + 3 * 4 * 32) * 4 <= STAGE * 2, "combine scratch fits");
 };
 
-template <int D>
+template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p) {
   using T = DTile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[T::STAGE];
+  // Paged cache: the page id of every row of the next tile to load, in two
+  // slots. Row r of tile t (starting at t0) reads slot t % 2, entry r - t0.
+  __shared__ int pid[PAGED ? 2 : 1][PAGED ? kBN : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -102,11 +116,27 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   }
 
   const size_t head_kv = ((size_t)b * p.Hkv + kvh) * p.Nk;
-  const uint16_t* kbase = p.k + head_kv * D;
-  const uint16_t* vbase = p.v + head_kv * D;
+  const int* table = PAGED ? p.block_table + (size_t)b * p.max_pages : nullptr;
+  const int page_mask = (1 << p.page_shift) - 1;
+  // Paged: thread tid < kBN reads the block-table entry of row t0 + tid (one
+  // iteration before the rows themselves are loaded, so the table read is off
+  // the load's critical path); rows past the chunk get -1.
+  auto fetch_pid = [&](int t0) -> int {
+    const int r = t0 + tid;
+    return (tid < kBN && r < hi) ? table[r >> p.page_shift] : -1;
+  };
+  // Element offset of cache row r (< hi) of tile t0 in page-id slot `slot`,
+  // and whether it may be read: a page id outside the pool reads as zeros.
+  auto row_at = [&](int r, int t0, int slot, bool& ok) -> size_t {
+    if (!PAGED) return (head_kv + (size_t)r) * D;
+    const int pg = pid[slot][r - t0];
+    ok = ok && (unsigned)pg < (unsigned)p.num_pages;
+    const size_t page = ok ? (size_t)pg : 0;
+    return (((page * p.Hkv + kvh) << p.page_shift) + (size_t)(r & page_mask)) * D;
+  };
 
   uint4 kreg[T::NB][4], vreg[T::NB][4];
-  auto load_tile = [&](int t0) {
+  auto load_tile = [&](int t0, int slot) {
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) {
       const int bi = tid + nb * kThreads;
@@ -115,9 +145,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int rk = t0 + kc_k * 4 + r;
-        kreg[nb][r] = load16(kbase + (size_t)(rk < hi ? rk : 0) * D + dc_k * 8, rk < hi);
+        bool okk = rk < hi;
+        const size_t ok_off = row_at(okk ? rk : t0, t0, slot, okk);
+        kreg[nb][r] = load16(p.k + ok_off + dc_k * 8, okk);
         const int rv = t0 + kc_v * 4 + r;
-        vreg[nb][r] = load16(vbase + (size_t)(rv < hi ? rv : 0) * D + dc_v * 8, rv < hi);
+        bool okv = rv < hi;
+        const size_t ov_off = row_at(okv ? rv : t0, t0, slot, okv);
+        vreg[nb][r] = load16(p.v + ov_off + dc_v * 8, okv);
       }
     }
   };
@@ -150,13 +184,25 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   float m_ref = -kInf;
   float l_b = 0.f, l_f = 0.f;  // row sums of the bf16-rounded and the fp32 P
 
-  if (ntiles > 0) load_tile(start);
+  int pid_next = -1;  // paged: page id of this thread's row of the tile after the next
+  if (ntiles > 0) {
+    if (PAGED) {
+      if (tid < kBN) pid[0][tid] = fetch_pid(start);
+      if (ntiles > 1) pid_next = fetch_pid(start + kBN);
+      __syncthreads();
+    }
+    load_tile(start, 0);
+  }
   for (int it = 0; it < ntiles; ++it) {
     const int t0 = start + it * kBN;
     __syncthreads();  // every wave is done with the previous tile
     store_tile();
+    if (PAGED && tid < kBN) pid[(it + 1) & 1][tid] = pid_next;  // rows of tile it + 1
     __syncthreads();
-    if (it + 1 < ntiles) load_tile(t0 + kBN);
+    if (it + 1 < ntiles) {
+      load_tile(t0 + kBN, (it + 1) & 1);
+      if (PAGED && it + 2 < ntiles) pid_next = fetch_pid(t0 + 2 * kBN);
+    }
 
     const uint16_t* ks = smem;
     const uint16_t* vs = smem + kBN * T::KSTR;
@@ -310,17 +356,28 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.S = a.splits;
   sp.window = a.window;
   sp.kv_lens = a.kv_lens;
+  sp.block_table = a.block_table;
+  sp.page_shift = 0;
+  while (a.block_table != nullptr && (1 << sp.page_shift) < a.page_size) ++sp.page_shift;
+  sp.max_pages = a.max_pages;
+  sp.num_pages = a.num_pages;
   sp.scale = a.scale;
   sp.scale_log2 = a.scale * kLog2e;
   sp.thr_raw = kRescaleThreshold / sp.scale_log2;
   const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * a.splits);
   if (log_enabled())
-    fprintf(stderr, "[miattn] decode d=%d splits=%d kv_lens=%s split_grid=%u merge_grid=%d\n",
-            a.d, a.splits, a.kv_lens != nullptr ? "per-sequence" : "uniform", nsplit_blk,
-            a.B * a.H);
+    fprintf(stderr,
+            "[miattn] decode d=%d splits=%d kv_lens=%s page_size=%d split_grid=%u "
+            "merge_grid=%d\n",
+            a.d, a.splits, a.kv_lens != nullptr ? "per-sequence" : "uniform",
+            a.block_table != nullptr ? a.page_size : 0, nsplit_blk, a.B * a.H);
   void* sargs[] = {&sp};
-  const void* sfn = a.d == 128 ? reinterpret_cast<const void*>(&decode_split_kernel<128>)
-                               : reinterpret_cast<const void*>(&decode_split_kernel<64>);
+  const bool paged = a.block_table != nullptr;
+  const void* sfn =
+      a.d == 128 ? (paged ? reinterpret_cast<const void*>(&decode_split_kernel<128, true>)
+                          : reinterpret_cast<const void*>(&decode_split_kernel<128, false>))
+                 : (paged ? reinterpret_cast<const void*>(&decode_split_kernel<64, true>)
+                          : reinterpret_cast<const void*>(&decode_split_kernel<64, false>));
   hipError_t e = hipLaunchKernel(sfn, dim3(nsplit_blk), dim3(kThreads), sargs, 0, stream);
   if (e != hipSuccess) return e;
 

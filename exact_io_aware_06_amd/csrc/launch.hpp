@@ -39,6 +39,11 @@ struct DecodeArgs {
   void* workspace;
   // Per-sequence cache lengths in [0, Nk] (null: every sequence holds Nk keys).
   const int* kv_lens;
+  // Paged cache (null: contiguous [B, Hkv, Nk, d] caches): k, v are page
+  // pools [num_pages, Hkv, page_size, d], block_table is [B, max_pages], and
+  // Nk = max_pages * page_size. page_size is a power of two.
+  const int* block_table;
+  int page_size, max_pages, num_pages;
 };
 
 // Query-tile rows / key-tile columns of the bf16 and fp32 forward kernels.

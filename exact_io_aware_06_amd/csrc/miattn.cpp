@@ -129,9 +129,12 @@ int resolve_splits(int B, int Hkv, int Nk, int num_splits) {
   return (int)want;
 }
 
+// Paged caches pass block_table != NULL with page_size / max_pages / num_pages
+// and Nk = max_pages * page_size; contiguous caches pass NULL and zeros.
 int run_decode(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
                void* o, float* lse, int B, int H, int Hkv, int Nk, int d, float scale,
                int window, int num_splits, void* workspace, size_t workspace_bytes,
+               const int* block_table, int page_size, int max_pages, int num_pages,
                void* stream) {
   if (B < 0 || H < 1 || Hkv < 1 || Nk < 0) return MIATTN_EINVAL;
   if (H % Hkv != 0) return MIATTN_EINVAL;
@@ -144,13 +147,16 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache, const in
     return MIATTN_EUNSUPPORTED;
   if (B == 0) return MIATTN_OK;
   if (q == nullptr || o == nullptr) return MIATTN_EINVAL;
-  if (Nk > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
+  const bool paged = block_table != nullptr;
+  if (!paged && Nk > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
+  if (paged && num_pages > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
   const size_t need = miattn::decode_workspace_bytes(B, H, d, S);
   if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
   int st = device_status();
   if (st != MIATTN_OK) return st;
-  DecodeArgs a{q,     k_cache, v_cache, o, lse,       B,      H,
-               Hkv,   Nk,      d,       scale, window, S, workspace, kv_lens};
+  DecodeArgs a{q,      k_cache, v_cache, o,         lse,     B,          H,
+               Hkv,    Nk,      d,       scale,     window,  S,          workspace,
+               kv_lens, block_table, page_size, max_pages, num_pages};
   return launch_status(miattn::launch_decode(a, static_cast<hipStream_t>(stream)));
 }
 
@@ -201,7 +207,7 @@ int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, 
                        float* lse, int B, int H, int Hkv, int Nk, int d, float scale, int window,
                        int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   return run_decode(q, k_cache, v_cache, nullptr, o, lse, B, H, Hkv, Nk, d, scale, window,
-                    num_splits, workspace, workspace_bytes, stream);
+                    num_splits, workspace, workspace_bytes, nullptr, 0, 0, 0, stream);
 }
 
 int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_cache,
@@ -210,7 +216,23 @@ int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_
                               void* workspace, size_t workspace_bytes, void* stream) {
   if (B > 0 && kv_lens == nullptr) return MIATTN_EINVAL;
   return run_decode(q, k_cache, v_cache, kv_lens, o, lse, B, H, Hkv, Nk, d, scale, window,
-                    num_splits, workspace, workspace_bytes, stream);
+                    num_splits, workspace, workspace_bytes, nullptr, 0, 0, 0, stream);
+}
+
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int* block_table, const int* kv_lens, void* o, float* lse, int B,
+                      int H, int Hkv, int d, int page_size, int num_pages, int max_pages,
+                      float scale, int window, int num_splits, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  if (page_size < 1 || page_size > 65536 || (page_size & (page_size - 1)) != 0)
+    return MIATTN_EINVAL;
+  if (num_pages < 0 || max_pages < 0) return MIATTN_EINVAL;
+  const long long nk = (long long)max_pages * page_size;
+  if (nk > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  if (B > 0 && (kv_lens == nullptr || block_table == nullptr)) return MIATTN_EINVAL;
+  return run_decode(q, k_pages, v_pages, kv_lens, o, lse, B, H, Hkv, (int)nk, d, scale, window,
+                    num_splits, workspace, workspace_bytes, block_table, page_size, max_pages,
+                    num_pages, stream);
 }
 
 int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,

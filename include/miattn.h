@@ -164,6 +164,34 @@ int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_
                               int num_splits, void* workspace, size_t workspace_bytes,
                               void* stream);
 
+/*
+ * Split-K decode over a paged KV cache ("Attention Research", section 2,
+ * names paged variants among the attention kernel libraries): the keys and
+ * values of all sequences live in fixed-size pages of one pool, and a block
+ * table says which physical page holds each sequence's j-th run of
+ * page_size keys. Only the address of a key row differs from
+ * attn_decode_splitk_varlen; the result is the same as for a contiguous cache
+ * holding the same keys.
+ *
+ * k_pages, v_pages: [num_pages, Hkv, page_size, d] bf16 (one page holds
+ * page_size consecutive keys of every KV head). block_table: DEVICE int32
+ * [B, max_pages]; key j of sequence b is row j % page_size of page
+ * block_table[b * max_pages + j / page_size]. kv_lens: DEVICE int32 [B],
+ * clamped to [0, max_pages * page_size]. Entries past a sequence's length
+ * are never read; an entry inside it that is outside [0, num_pages) reads as
+ * zero keys and values (a meaningless result, but nothing outside the pool
+ * is touched). Pages may be shared between sequences.
+ * page_size: a power of two in [1, 65536], else MIATTN_EINVAL.
+ * workspace: attn_decode_workspace_bytes(B, H, Hkv, max_pages * page_size, d,
+ * num_splits) bytes. q, o, lse, scale, window, num_splits as for
+ * attn_decode_splitk.
+ */
+int attn_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                      const int* block_table, const int* kv_lens, void* o, float* lse,
+                      int B, int H, int Hkv, int d, int page_size, int num_pages,
+                      int max_pages, float scale, int window, int num_splits,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* The split count attn_decode_splitk uses for these arguments (resolves 0),
  * or a negative status for invalid ones. */
 int attn_decode_num_splits(int B, int Hkv, int Nk, int num_splits);

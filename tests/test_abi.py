@@ -42,7 +42,7 @@ def test_header_declares_expected_entry_points():
     for n in ["attn_fwd", "attn_fwd_f32", "attn_decode_splitk", "attn_decode_workspace_bytes",
               "attn_strerror", "attn_fwd_tile_shape", "attn_fwd_tile_counts",
               "attn_decode_num_splits", "attn_fwd_varlen", "attn_fwd_varlen_tile_counts",
-              "attn_decode_splitk_varlen"]:
+              "attn_decode_splitk_varlen", "attn_decode_paged"]:
         assert n in names
 
 
@@ -196,6 +196,33 @@ def test_decode_varlen_invalid_arguments(lib):
     assert vdec(lib, B=0, lens=NULL, q=NULL, k=NULL, v=NULL, o=NULL, ws=NULL) == OK
 
 
+def pdec(lib, table=FAKE, lens=FAKE, B=2, ps=16, npg=10, maxp=4, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, H=8, Hkv=2, d=128, scale=0.1, window=0,
+             splits=2, ws=FAKE, ws_bytes=1 << 30)
+    a.update(kw)
+    return lib.attn_decode_paged(a["q"], a["k"], a["v"], table, lens, a["o"], a["lse"], B,
+                                 a["H"], a["Hkv"], a["d"], ps, npg, maxp,
+                                 ctypes.c_float(a["scale"]), a["window"], a["splits"], a["ws"],
+                                 a["ws_bytes"], NULL)
+
+
+def test_decode_paged_invalid_arguments(lib):
+    assert pdec(lib, table=NULL) == EINVAL
+    assert pdec(lib, lens=NULL) == EINVAL
+    assert pdec(lib, ps=0) == EINVAL
+    assert pdec(lib, ps=24) == EINVAL          # not a power of two
+    assert pdec(lib, ps=1 << 17) == EINVAL
+    assert pdec(lib, npg=-1) == EINVAL
+    assert pdec(lib, maxp=-1) == EINVAL
+    assert pdec(lib, k=NULL) == EINVAL
+    assert pdec(lib, q=NULL) == EINVAL
+    assert pdec(lib, splits=65) == EINVAL      # more splits than keys (4 pages x 16)
+    assert pdec(lib, d=96) == EUNSUP
+    assert pdec(lib, ps=65536, maxp=1 << 16) == EUNSUP   # capacity past 2^31 keys
+    assert pdec(lib, ws_bytes=10) == EWS
+    assert pdec(lib, B=0, table=NULL, lens=NULL, q=NULL, o=NULL, ws=NULL) == OK
+
+
 def _no_gpu():
     try:
         import torch
@@ -211,3 +238,4 @@ def test_valid_call_without_device_reports_nodevice(lib):
     assert dec(lib) == ENODEV
     assert vfwd(lib) == ENODEV
     assert vdec(lib) == ENODEV
+    assert pdec(lib) == ENODEV
