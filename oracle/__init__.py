@@ -21,6 +21,8 @@ Modules:
   online     - the pages' online-softmax recurrence and the split-K merge, as
                independent fp64 models used only to pin the definition
   tiles      - which (query-tile, key-tile) blocks hold any visible pair
+  backward   - gradients dq, dk, dv of the definition (chain rule through the
+               materialised softmax)
   varlen     - packed documents (block-diagonal mask), decode over caches
                of per-sequence length and over paged caches
 """
@@ -33,6 +35,7 @@ from .attention import (  # noqa: F401
     decode_ref,
     decode_rows_ref,
 )
+from .backward import attention_bwd_ref  # noqa: F401
 from .online import online_softmax_model, split_partials_ref, merge_ref  # noqa: F401
 from .tiles import tiles_needed  # noqa: F401
 from .varlen import (  # noqa: F401
