@@ -13,6 +13,8 @@ from .api import (  # noqa: F401
     attn_decode,
     attn_decode_varlen,
     attn_decode_paged,
+    attn_bwd,
+    bwd_workspace_bytes,
     decode_workspace_bytes,
     fwd_tile_counts,
     fwd_varlen_tile_counts,

@@ -62,6 +62,10 @@ def load_library():
         lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P,
                                           S, P]
         lib.attn_decode_paged.restype = I
+        lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+        lib.attn_bwd_workspace_bytes.restype = S
+        lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, S, P]
+        lib.attn_bwd.restype = I
         lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
         lib.attn_fwd_tile_shape.restype = I
         lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -361,6 +365,43 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale=None, win
                                      int(window), int(num_splits), _ptr(workspace),
                                      ctypes.c_size_t(workspace.numel()), _stream(q.device)))
     return out, lse
+
+
+def bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d) -> int:
+    return int(load_library().attn_bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d))
+
+
+def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, window=0, dq=None, dk=None,
+             dv=None, workspace=None):
+    """Backward of attn_fwd (bf16): returns (dq like q, dk like k, dv like v).
+
+    o and lse are attn_fwd's outputs for the same q, k, v, scale, causal and
+    window; dout is the upstream gradient [B, H, Nq, d] bf16.
+    """
+    import torch
+    B, H, Hkv, Nq, Nk, d = _fwd_checks(q, k, v)
+    _require(q.dtype == torch.bfloat16, "the backward takes bfloat16")
+    for t, name in ((o, "o"), (dout, "dout")):
+        _require(t.shape == q.shape and t.dtype == q.dtype and t.device == q.device
+                 and t.is_contiguous(), f"{name} must match q")
+    _require(lse.shape == (B, H, Nq) and lse.dtype == torch.float32 and lse.device == q.device
+             and lse.is_contiguous(), "lse must be fp32 [B, H, Nq]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _require(t.shape == ref.shape and t.dtype == ref.dtype and t.is_contiguous(), f"bad {name}")
+    lib = load_library()
+    nbytes = int(lib.attn_bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
+                            _ptr(dk), _ptr(dv), B, H, Hkv, Nq, Nk, d, ctypes.c_float(scale),
+                            int(bool(causal)), int(window), _ptr(workspace),
+                            ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+    return dq, dk, dv
 
 
 def calib_mfma(blocks: int, iters: int, sink):

@@ -22,7 +22,7 @@ CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libmiattn.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
-SOURCES = ["miattn.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "calib.hip"]
+SOURCES = ["miattn.cpp", "fwd_bf16.hip", "fwd_f32.hip", "decode.hip", "bwd.hip", "calib.hip"]
 ARCH = "gfx950"
 
 COMMON_FLAGS = [

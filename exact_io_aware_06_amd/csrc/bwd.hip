@@ -1,0 +1,704 @@
+// Attention backward, bf16 in / bf16 out, fp32 accumulation, gfx950.
+//
+// The attention matrix is recomputed from Q, K and the forward's LSE instead
+// of being stored ("Quadratic Complexity Bottleneck", FlashAttention entry;
+// "Chapter 3.1 - The Cost of Attention", section 5). With P = exp(S - LSE),
+// S = scale Q K^T (masked), and D = rowsum(dO * O):
+//
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
+//   dK = scale dS^T Q.
+//
+// Four kernels, no atomics (every output element has exactly one writer, so
+// results are deterministic):
+//   bwd_prep  D for every query row (reads dO and O once).
+//   bwd_dq    one work-group per (batch, head, 128 query rows), four waves of
+//             32 rows, streaming the visible 64-key K/V tiles through LDS:
+//             S^T = K Q^T and dP^T = V dO^T on matrix cores (Q, dO stay in
+//             registers), dS^T on the vector ALU, then dQ^T += K^T dS^T with
+//             dS^T straight from registers and K^T gathered by transposing LDS
+//             reads. The same structure as the forward kernel.
+//   bwd_dkdv  one work-group per (batch, query head, 128 keys), four waves of
+//             32 keys; K stays in registers and V in LDS while 32-row Q / dO
+//             tiles stream through LDS: S = Q K^T and dP = dO V^T, then
+//             dV^T += dO^T P and dK^T += Q^T dS with P, dS straight from
+//             registers. Each query head writes its own dK, dV (bf16 when the
+//             K/V head has one query head, fp32 partials otherwise).
+//   bwd_gsum  sums the fp32 partials over the G query heads of each K/V head
+//             (GQA) and rounds to bf16.
+// Splitting dK/dV work by query head keeps the causal work per work-group
+// balanced enough (heaviest key tiles first) with no cross-work-group
+// reduction other than the small group sum.
+
+#include <cstdio>
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace miattn {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+// An LDS tile of ROWS rows x D bf16, row-major, 16-byte chunks of each row
+// XOR-swizzled, filled by 1 KB global-to-LDS blocks (64 lanes x 16 bytes).
+template <int D, int ROWS>
+struct LTile {
+  static constexpr int ROWB = D * 2;
+  static constexpr int CPR = D / 8;
+  static constexpr int RPB = 64 / CPR;
+  static constexpr int BYTES = ROWS * ROWB;
+  static constexpr int NBLK = BYTES / 1024;
+  static constexpr int BPW = NBLK / 4;
+  static_assert(NBLK % 4 == 0, "DMA blocks split over four waves");
+};
+
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
+  return (r >> 1) & 7;
+}
+
+// Per-lane LDS byte offsets into such a tile.
+//  row_off: matrix-core operand "row l32, k = 16 ks + 8 g .. + 8" (add
+//           32 * rb * ROWB for row block rb).
+//  tr_off:  transposing reads giving "column (dim) db*32 + l32, rows
+//           16 tt + {4g..4g+3, 8+4g..8+4g+3}" (add 16 * tt * ROWB), the row
+//           order the matrix-core result registers hold.
+//  dma_off: this lane's slot in the wave's DMA blocks.
+template <int D>
+struct LOffsets {
+  uint32_t row_off[D / 16];
+  uint32_t tr_off[D / 32][2];
+  __device__ __forceinline__ void init(int lane) {
+    const int l32 = lane & 31, g = lane >> 5;
+    const int sw = swz<D>(l32);
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks)
+      row_off[ks] = (uint32_t)(l32 * D * 2 + (((2 * ks + g) ^ sw) << 4));
+    const int j = lane & 15, a = j & 3, e = j >> 2, hh = (lane >> 4) & 1;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int r = 4 * g + e + 8 * qh;
+      const int rs = swz<D>(r);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const int c = 4 * db + 2 * hh + (a >> 1);
+        tr_off[db][qh] = (uint32_t)(r * D * 2 + ((c ^ rs) << 4) + (a & 1) * 8);
+      }
+    }
+  }
+};
+
+template <int D, int ROWS>
+__device__ __forceinline__ uint32_t dma_off(int wave, int lane, int i) {
+  using T = LTile<D, ROWS>;
+  const int blk = wave * T::BPW + i;
+  const int r = blk * T::RPB + lane / T::CPR;
+  return (uint32_t)(r * T::ROWB + (((lane % T::CPR) ^ swz<D>(r)) << 4));
+}
+
+// DMA rows [r0, r0 + ROWS) of a row-major [n, D] bf16 array into an LDS tile;
+// rows at or past n read as zero.
+template <int D, int ROWS>
+__device__ __forceinline__ void dma_rows(const uint16_t* base, long long r0, long long n,
+                                         lds_u8* dst, const uint32_t* doff, int wave) {
+  using T = LTile<D, ROWS>;
+  const uint32_t bytes = r0 < n ? (uint32_t)((n - r0) * T::ROWB) : 0u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + r0 * D, bytes);
+#pragma unroll
+  for (int i = 0; i < T::BPW; ++i) dma16(rs, dst + (wave * T::BPW + i) * 1024, doff[i]);
+}
+
+// V^T-style operand: two transposing reads of an LDS tile.
+__device__ __forceinline__ bf16x8 tr_operand(const lds_u8* tile, uint32_t o0, uint32_t o1) {
+  const uint2 lo = lds_tr_b64(tile, o0);
+  const uint2 hi = lds_tr_b64(tile, o1);
+  return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+struct BwdParams {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* o;
+  const uint16_t* dout;
+  const float* lse;
+  float* delta;  // [B, H, Nq]
+  uint16_t* dq;
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dk_part;  // [B, H, Nk, d] when G > 1
+  float* dv_part;
+  int B, H, Hkv, Nq, Nk, G;
+  float scale, scale_log2;
+  int causal, window;
+  int nqt, nkt;
+  int xcd_remap;
+};
+
+// ---------------------------------------------------------------------------
+// D = rowsum(dO * O), fp32, over the stored (bf16) O.
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p, long long rows) {
+  constexpr int TPR = D / 8;  // lanes per row, 8 elements each
+  constexpr int RPB = kThreads / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int c = (threadIdx.x % TPR) * 8;
+  const bool ok = row < rows;
+  const uint4 a = load16(p.dout + (ok ? row : 0) * D + c, ok);
+  const uint4 b = load16(p.o + (ok ? row : 0) * D + c, ok);
+  const bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s = __builtin_fmaf((float)x[i], (float)y[i], s);
+#pragma unroll
+  for (int w = TPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, 64);
+  if (ok && threadIdx.x % TPR == 0) p.delta[row] = s;
+}
+
+// ---------------------------------------------------------------------------
+// dQ.
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
+  using KT = LTile<D, 64>;
+  constexpr int BN = 64, KB = 2, KS = D / 16, DB = D / 32, PS = BN / 16;
+  // K ring of two tiles at [0, 2 BYTES), V ring at [2 BYTES, 4 BYTES).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * KT::BYTES];
+  lds_u8* const L = lds_ptr(smem);
+  constexpr int KRING = 0, VRING = 2 * KT::BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // Work-group -> (b, h, query tile): heaviest causal tiles first; with
+  // (B * Hkv) % 8 == 0 the work-groups of one K/V head share one XCD.
+  int b, h, qt;
+  {
+    const int id = blockIdx.x;
+    if (p.xcd_remap) {
+      const int xcd = id & 7, slot = id >> 3;
+      const int per_rank = ((p.B * p.Hkv) >> 3) * p.G;
+      const int rank = slot / per_rank, rem = slot - rank * per_rank;
+      const int ul = rem / p.G, gh = rem - ul * p.G;
+      const int u = ul * 8 + xcd;
+      b = u / p.Hkv;
+      h = (u - b * p.Hkv) * p.G + gh;
+      qt = p.nqt - 1 - rank;
+    } else {
+      const int bh = p.B * p.H, rank = id / bh, rem = id - rank * bh;
+      b = rem / p.H;
+      h = rem - b * p.H;
+      qt = p.nqt - 1 - rank;
+    }
+  }
+  const int kvh = h / p.G;
+  const int q0 = qt * 128;
+  const int off = p.Nk - p.Nq;
+  const int q_last = min(q0 + 128, p.Nq) - 1;
+  const long long p_lo = (long long)q0 + off, p_hi = (long long)q_last + off;
+  long long key_lo = 0, key_hi = p.Nk;
+  if (p.causal) key_hi = min(key_hi, p_hi + 1);
+  else if (p.window > 0) key_hi = min(key_hi, p_hi + p.window + 1);
+  if (p.window > 0) key_lo = max(key_lo, p_lo - p.window);
+  const int kt_lo = key_hi > key_lo ? (int)(key_lo / BN) : 0;
+  const int kt_hi = key_hi > key_lo ? (int)((key_hi + BN - 1) / BN) : 0;
+  const int ntiles = kt_hi - kt_lo;
+
+  const int qrow = q0 + wave * 32 + l32;
+  const bool qvalid = qrow < p.Nq;
+  const long long qpos = (long long)qrow + off;
+  const long long lo_q = p.window > 0 ? qpos - p.window : 0;
+  long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)p.Nk - 1);
+  hi_q = min(hi_q, (long long)p.Nk - 1);
+  const size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+
+  bf16x8 qf[KS], df[KS];
+  {
+    const size_t r = (head_q + (qvalid ? qrow : 0)) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      qf[ks] = as_bf16x8(load16(p.q + r + ks * 16, qvalid));
+      df[ks] = as_bf16x8(load16(p.dout + r + ks * 16, qvalid));
+    }
+  }
+  // exp2-domain LSE of this row (+inf for a row that sees no key, so every
+  // P of it is 0) and its D.
+  const float lse_row = qvalid ? p.lse[head_q + qrow] : -kInf;
+  const float lse2 = lse_row == -kInf ? kInf : lse_row * kLog2e;
+  const float dlt = qvalid ? p.delta[head_q + qrow] : 0.f;
+
+  LOffsets<D> lo;
+  lo.init(lane);
+  uint32_t doff[KT::BPW];
+#pragma unroll
+  for (int i = 0; i < KT::BPW; ++i) doff[i] = dma_off<D, 64>(wave, lane, i);
+
+  const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
+  const uint16_t* kbase = p.k + head_kv * D;
+  const uint16_t* vbase = p.v + head_kv * D;
+
+  auto tile_partial = [&](int kt) -> bool {
+    const long long k0 = (long long)kt * BN, k1 = k0 + BN - 1;
+    if (k1 >= p.Nk) return true;
+    if (p.causal && k1 > p_lo) return true;
+    if (p.window > 0) {
+      if (k0 < p_hi - p.window) return true;
+      if (!p.causal && k1 > p_lo + p.window) return true;
+    }
+    return false;
+  };
+
+  f32x16 acc[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
+
+  if (ntiles > 0) {
+    dma_rows<D, 64>(kbase, (long long)kt_lo * BN, p.Nk, L + KRING, doff, wave);
+    dma_rows<D, 64>(vbase, (long long)kt_lo * BN, p.Nk, L + VRING, doff, wave);
+    wait_vmem();
+    __syncthreads();
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    const int kt = kt_lo + t;
+    const int slot = t & 1;
+    if (t + 1 < ntiles) {
+      dma_rows<D, 64>(kbase, (long long)(kt + 1) * BN, p.Nk, L + KRING + (1 - slot) * KT::BYTES,
+                      doff, wave);
+      dma_rows<D, 64>(vbase, (long long)(kt + 1) * BN, p.Nk, L + VRING + (1 - slot) * KT::BYTES,
+                      doff, wave);
+    }
+    const lds_u8* kt_lds = L + KRING + slot * KT::BYTES;
+    const lds_u8* vt_lds = L + VRING + slot * KT::BYTES;
+
+    // S^T = K Q^T and dP^T = V dO^T (keys as rows, this wave's rows as columns).
+    f32x16 s[KB], dp[KB];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const uint32_t o = lo.row_off[ks] + kb * 32 * KT::ROWB;
+        s[kb] = mfma32x32x16(lds_b128(kt_lds, o), qf[ks], s[kb]);
+        dp[kb] = mfma32x32x16(lds_b128(vt_lds, o), df[ks], dp[kb]);
+      }
+    }
+    mfma_drain();
+
+    if (tile_partial(kt)) {
+      const long long base = (long long)kt * BN + 4 * g;
+      const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
+      const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          s[kb][r] = ((c >= rl) & (c <= rh)) ? s[kb][r] : -kInf;
+        }
+    }
+
+    // dS^T = P^T * (dP^T - D), rounded to bf16 as the next product's operand.
+    bf16x8 dsf[PS];
+#pragma unroll
+    for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x8 ds;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float pv = fast_exp2(__builtin_fmaf(s[kb][hf * 8 + i], p.scale_log2, -lse2));
+          ds[i] = pv * (dp[kb][hf * 8 + i] - dlt);
+        }
+        dsf[kb * 2 + hf] = to_bf16x8(ds);
+      }
+
+    // dQ^T += K^T dS^T.
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int tt = 0; tt < PS; ++tt)
+        acc[db] = mfma32x32x16(
+            tr_operand(kt_lds, lo.tr_off[db][0] + tt * 16 * KT::ROWB,
+                       lo.tr_off[db][1] + tt * 16 * KT::ROWB),
+            dsf[tt], acc[db]);
+
+    wait_vmem();
+    __syncthreads();
+  }
+  mfma_drain();
+
+  if (qvalid) {
+    uint16_t* op = p.dq + (head_q + qrow) * D + 4 * g;
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr) {
+        uint2 w;
+        w.x = pack_bf16x2(acc[db][rr * 4 + 0] * p.scale, acc[db][rr * 4 + 1] * p.scale);
+        w.y = pack_bf16x2(acc[db][rr * 4 + 2] * p.scale, acc[db][rr * 4 + 3] * p.scale);
+        *reinterpret_cast<uint2*>(op + db * 32 + rr * 8) = w;
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dK, dV.
+
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
+  using QT = LTile<D, 32>;   // one 32-row Q (or dO) step
+  using VT = LTile<D, 128>;  // the work-group's V tile
+  constexpr int KS = D / 16, DB = D / 32;
+  // LDS: V tile, then the Q ring (2 steps) and the dO ring (2 steps).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[VT::BYTES + 4 * QT::BYTES];
+  __shared__ __attribute__((aligned(16))) float stat[2][2][32];  // [slot][lse2, D][row]
+  lds_u8* const L = lds_ptr(smem);
+  constexpr int VOFF = 0, QRING = VT::BYTES, DRING = VT::BYTES + 2 * QT::BYTES;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, g = lane >> 5;
+
+  // Work-group -> (b, h, key tile): lowest key tiles (most visible query
+  // rows under a causal mask) first; with (B * H) % 8 == 0 the work-groups
+  // of one query head share one XCD (their Q / dO streams overlap).
+  int b, h, kt;
+  {
+    const int id = blockIdx.x;
+    const int bh = p.B * p.H;
+    if (p.xcd_remap) {
+      const int xcd = id & 7, slot = id >> 3;
+      const int per_rank = bh >> 3;
+      const int rank = slot / per_rank, ul = slot - rank * per_rank;
+      const int u = ul * 8 + xcd;
+      b = u / p.H;
+      h = u - b * p.H;
+      kt = rank;
+    } else {
+      const int rank = id / bh, rem = id - rank * bh;
+      b = rem / p.H;
+      h = rem - b * p.H;
+      kt = rank;
+    }
+  }
+  const int kvh = h / p.G;
+  const int k0 = kt * 128;
+  const int k1 = min(k0 + 127, p.Nk - 1);
+  const int off = p.Nk - p.Nq;
+
+  // Query rows that see any key of [k0, k1]; steps of 32 rows over them.
+  long long i_lo = 0, i_hi = (long long)p.Nq - 1;
+  if (p.causal) {
+    i_lo = (long long)k0 - off;
+    if (p.window > 0) i_hi = min(i_hi, (long long)k1 + p.window - off);
+  } else if (p.window > 0) {
+    i_lo = (long long)k0 - p.window - off;
+    i_hi = min(i_hi, (long long)k1 + p.window - off);
+  }
+  i_lo = max(i_lo, 0LL);
+  const int st_lo = i_hi >= i_lo ? (int)(i_lo / 32) : 0;
+  const int nsteps = i_hi >= i_lo ? (int)(i_hi / 32) + 1 - st_lo : 0;
+
+  // This lane's key and the query rows that see it: [jq_lo, jq_hi].
+  const int key = k0 + wave * 32 + l32;
+  const bool kvalid = key < p.Nk;
+  long long jq_lo = 0, jq_hi = (long long)p.Nq - 1;
+  if (p.causal) {
+    jq_lo = (long long)key - off;
+    if (p.window > 0) jq_hi = (long long)key + p.window - off;
+  } else if (p.window > 0) {
+    jq_lo = (long long)key - p.window - off;
+    jq_hi = (long long)key + p.window - off;
+  }
+
+  const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
+  const size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+  // K as the B operand of S = Q K^T (k = dims), kept in registers.
+  bf16x8 kf[KS];
+  {
+    const size_t r = (head_kv + (kvalid ? key : 0)) * D + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) kf[ks] = as_bf16x8(load16(p.k + r + ks * 16, kvalid));
+  }
+
+  LOffsets<D> lo;
+  lo.init(lane);
+  uint32_t qdoff[QT::BPW], vdoff[VT::BPW];
+#pragma unroll
+  for (int i = 0; i < QT::BPW; ++i) qdoff[i] = dma_off<D, 32>(wave, lane, i);
+#pragma unroll
+  for (int i = 0; i < VT::BPW; ++i) vdoff[i] = dma_off<D, 128>(wave, lane, i);
+
+  const uint16_t* qbase = p.q + head_q * D;
+  const uint16_t* dbase = p.dout + head_q * D;
+
+  // exp2-domain LSE and D of query row r (rows past Nq or seeing no key:
+  // +inf, so every P of the row is 0).
+  auto row_stats = [&](int r, float& l2, float& dl) {
+    const bool ok = r < p.Nq;
+    const float l = ok ? p.lse[head_q + r] : -kInf;
+    l2 = l == -kInf ? kInf : l * kLog2e;
+    dl = ok ? p.delta[head_q + r] : 0.f;
+  };
+  // Does step st (rows [32 st, 32 st + 32)) need the per-element mask?
+  auto step_partial = [&](int st) -> bool {
+    const long long s0 = (long long)st * 32 + off, s1 = s0 + 31;  // positions
+    if (p.causal) {
+      if (s0 < k1) return true;
+      if (p.window > 0 && s1 - p.window > k0) return true;
+    } else if (p.window > 0) {
+      if (s1 - p.window > k0 || s0 + p.window < k1) return true;
+    }
+    return false;
+  };
+
+  f32x16 dka[DB], dva[DB];
+#pragma unroll
+  for (int i = 0; i < DB; ++i) {
+    dka[i] = f32x16{};
+    dva[i] = f32x16{};
+  }
+
+  if (nsteps > 0) {
+    dma_rows<D, 128>(p.v + head_kv * D, k0, p.Nk, L + VOFF, vdoff, wave);
+    dma_rows<D, 32>(qbase, (long long)st_lo * 32, p.Nq, L + QRING, qdoff, wave);
+    dma_rows<D, 32>(dbase, (long long)st_lo * 32, p.Nq, L + DRING, qdoff, wave);
+    if (tid < 32) row_stats(st_lo * 32 + tid, stat[0][0][tid], stat[0][1][tid]);
+    wait_vmem();
+    __syncthreads();
+  }
+  float nl2 = 0.f, ndl = 0.f;  // next step's row stats (threads < 32)
+  for (int t = 0; t < nsteps; ++t) {
+    const int st = st_lo + t;
+    const int slot = t & 1;
+    if (t + 1 < nsteps) {
+      dma_rows<D, 32>(qbase, (long long)(st + 1) * 32, p.Nq, L + QRING + (1 - slot) * QT::BYTES,
+                      qdoff, wave);
+      dma_rows<D, 32>(dbase, (long long)(st + 1) * 32, p.Nq, L + DRING + (1 - slot) * QT::BYTES,
+                      qdoff, wave);
+      if (tid < 32) row_stats((st + 1) * 32 + tid, nl2, ndl);
+    }
+    const lds_u8* q_lds = L + QRING + slot * QT::BYTES;
+    const lds_u8* d_lds = L + DRING + slot * QT::BYTES;
+    const lds_u8* v_lds = L + VOFF;
+
+    // S = Q K^T and dP = dO V^T (query rows as rows, this wave's keys as
+    // columns): lane (g, l32) holds key l32 for rows 8 c + 4 g + (0..3).
+    f32x16 s = f32x16{}, dp = f32x16{};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      s = mfma32x32x16(lds_b128(q_lds, lo.row_off[ks]), kf[ks], s);
+      // V operand: row (key) wave*32 + l32, dims 16 ks + 8 g .. + 8
+      dp = mfma32x32x16(lds_b128(d_lds, lo.row_off[ks]),
+                        lds_b128(v_lds, lo.row_off[ks] + wave * 32 * VT::ROWB), dp);
+    }
+    mfma_drain();
+
+    if (step_partial(st)) {
+      const long long base = (long long)st * 32 + 4 * g;  // row of register 0
+      const int rl = (int)max(min(jq_lo - base, 33LL), -1LL);
+      const int rh = (int)max(min(jq_hi - base, 33LL), -1LL);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int c = 8 * (r >> 2) + (r & 3);
+        s[r] = ((c >= rl) & (c <= rh)) ? s[r] : -kInf;
+      }
+    }
+
+    // P and dS, rounded to bf16 as operands of the two products below.
+    bf16x8 pf[2], dsf[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      f32x8 pv, ds;
+#pragma unroll
+      for (int c2 = 0; c2 < 2; ++c2) {
+        const int c = hf * 2 + c2;  // rows 8 c + 4 g + (0..3)
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[slot][0][8 * c + 4 * g]);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[slot][1][8 * c + 4 * g]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = c * 4 + e;
+          const float pr = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -l2[e]));
+          pv[c2 * 4 + e] = pr;
+          ds[c2 * 4 + e] = pr * (dp[r] - dl[e]);
+        }
+      }
+      pf[hf] = to_bf16x8(pv);
+      dsf[hf] = to_bf16x8(ds);
+    }
+
+    // dV^T += dO^T P and dK^T += Q^T dS (dims as rows, keys as columns).
+#pragma unroll
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t o0 = lo.tr_off[db][0] + tt * 16 * QT::ROWB;
+        const uint32_t o1 = lo.tr_off[db][1] + tt * 16 * QT::ROWB;
+        dva[db] = mfma32x32x16(tr_operand(d_lds, o0, o1), pf[tt], dva[db]);
+        dka[db] = mfma32x32x16(tr_operand(q_lds, o0, o1), dsf[tt], dka[db]);
+      }
+
+    if (t + 1 < nsteps && tid < 32) {
+      stat[1 - slot][0][tid] = nl2;
+      stat[1 - slot][1][tid] = ndl;
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  mfma_drain();
+
+  // Lane (g, l32) holds key `key`, dims db*32 + 8 rr + 4 g + (0..3).
+  if (kvalid) {
+    if (p.G == 1) {
+      uint16_t* kp = p.dk + (head_kv + key) * D + 4 * g;
+      uint16_t* vp = p.dv + (head_kv + key) * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          uint2 wk, wv;
+          wk.x = pack_bf16x2(dka[db][rr * 4 + 0] * p.scale, dka[db][rr * 4 + 1] * p.scale);
+          wk.y = pack_bf16x2(dka[db][rr * 4 + 2] * p.scale, dka[db][rr * 4 + 3] * p.scale);
+          wv.x = pack_bf16x2(dva[db][rr * 4 + 0], dva[db][rr * 4 + 1]);
+          wv.y = pack_bf16x2(dva[db][rr * 4 + 2], dva[db][rr * 4 + 3]);
+          *reinterpret_cast<uint2*>(kp + db * 32 + rr * 8) = wk;
+          *reinterpret_cast<uint2*>(vp + db * 32 + rr * 8) = wv;
+        }
+    } else {
+      const size_t part = ((size_t)(b * p.H + h) * p.Nk + key) * D + 4 * g;
+      float* kp = p.dk_part + part;
+      float* vp = p.dv_part + part;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr) {
+          const int r = rr * 4;
+          *reinterpret_cast<f32x4*>(kp + db * 32 + rr * 8) =
+              f32x4{dka[db][r] * p.scale, dka[db][r + 1] * p.scale, dka[db][r + 2] * p.scale,
+                    dka[db][r + 3] * p.scale};
+          *reinterpret_cast<f32x4*>(vp + db * 32 + rr * 8) =
+              f32x4{dva[db][r], dva[db][r + 1], dva[db][r + 2], dva[db][r + 3]};
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// GQA: dK, dV of a K/V head = sum over its G query heads' partials.
+
+__global__ __launch_bounds__(kThreads) void bwd_gsum_kernel(BwdParams p, int d, long long n8) {
+  const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;  // 8-element group
+  if (i >= n8) return;
+  const long long per_head = (long long)p.Nk * d / 8;
+  const long long bkv = i / per_head, rem = i - bkv * per_head;
+  const long long b = bkv / p.Hkv, kvh = bkv - b * p.Hkv;
+  f32x8 sk = {}, sv = {};
+  for (int gh = 0; gh < p.G; ++gh) {
+    const size_t src = ((size_t)(b * p.H + kvh * p.G + gh) * p.Nk * d) + (size_t)rem * 8;
+    const f32x4* kp = reinterpret_cast<const f32x4*>(p.dk_part + src);
+    const f32x4* vp = reinterpret_cast<const f32x4*>(p.dv_part + src);
+    const f32x4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      sk[e] += k0[e];
+      sk[e + 4] += k1[e];
+      sv[e] += v0[e];
+      sv[e + 4] += v1[e];
+    }
+  }
+  const size_t dst = (size_t)i * 8;
+  uint4 wk, wv;
+  wk.x = pack_bf16x2(sk[0], sk[1]);
+  wk.y = pack_bf16x2(sk[2], sk[3]);
+  wk.z = pack_bf16x2(sk[4], sk[5]);
+  wk.w = pack_bf16x2(sk[6], sk[7]);
+  wv.x = pack_bf16x2(sv[0], sv[1]);
+  wv.y = pack_bf16x2(sv[2], sv[3]);
+  wv.z = pack_bf16x2(sv[4], sv[5]);
+  wv.w = pack_bf16x2(sv[6], sv[7]);
+  *reinterpret_cast<uint4*>(p.dk + dst) = wk;
+  *reinterpret_cast<uint4*>(p.dv + dst) = wv;
+}
+
+template <int D>
+hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
+  void* args[] = {&prm};
+  hipError_t e = hipSuccess;
+  const long long rows = (long long)prm.B * prm.H * prm.Nq;
+  if (rows > 0) {
+    constexpr int RPB = kThreads / (D / 8);
+    void* pargs[] = {&prm, const_cast<long long*>(&rows)};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel<D>),
+                        dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), pargs, 0, stream);
+    if (e != hipSuccess) return e;
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),
+                        dim3((unsigned)((size_t)prm.B * prm.H * prm.nqt)), dim3(kThreads), args,
+                        0, stream);
+    if (e != hipSuccess) return e;
+  }
+  const size_t nkv = (size_t)prm.B * prm.H * prm.nkt;
+  if (nkv == 0) return hipSuccess;
+  // the dK / dV kernel groups work-groups by query head per XCD
+  prm.xcd_remap = ((prm.B * prm.H) % 8 == 0) ? 1 : 0;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>), dim3((unsigned)nkv),
+                      dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess || prm.G == 1) return e;
+  long long n8 = (long long)prm.B * prm.Hkv * prm.Nk * D / 8;
+  int d = D;
+  void* gargs[] = {&prm, &d, &n8};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gsum_kernel),
+                         dim3((unsigned)((n8 + kThreads - 1) / kThreads)), dim3(kThreads), gargs,
+                         0, stream);
+}
+
+}  // namespace
+
+size_t bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  const size_t delta = ((size_t)B * H * Nq * sizeof(float) + 255) / 256 * 256;
+  const size_t part = (H / Hkv > 1) ? (size_t)B * H * Nk * d * sizeof(float) : 0;
+  return delta + 2 * part;
+}
+
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
+  BwdParams p;
+  p.q = static_cast<const uint16_t*>(a.q);
+  p.k = static_cast<const uint16_t*>(a.k);
+  p.v = static_cast<const uint16_t*>(a.v);
+  p.o = static_cast<const uint16_t*>(a.o);
+  p.dout = static_cast<const uint16_t*>(a.dout);
+  p.lse = a.lse;
+  p.dq = static_cast<uint16_t*>(a.dq);
+  p.dk = static_cast<uint16_t*>(a.dk);
+  p.dv = static_cast<uint16_t*>(a.dv);
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  const size_t delta = ((size_t)a.B * a.H * a.Nq * sizeof(float) + 255) / 256 * 256;
+  p.delta = reinterpret_cast<float*>(ws);
+  p.dk_part = reinterpret_cast<float*>(ws + delta);
+  p.dv_part = p.dk_part + (size_t)a.B * a.H * a.Nk * a.d;
+  p.B = a.B;
+  p.H = a.H;
+  p.Hkv = a.Hkv;
+  p.Nq = a.Nq;
+  p.Nk = a.Nk;
+  p.G = a.H / a.Hkv;
+  p.scale = a.scale;
+  p.scale_log2 = a.scale * kLog2e;
+  p.causal = a.causal;
+  p.window = a.window;
+  p.nqt = (a.Nq + 127) / 128;
+  p.nkt = (a.Nk + 127) / 128;
+  p.xcd_remap = ((a.B * a.Hkv) % 8 == 0) ? 1 : 0;
+  if (log_enabled())
+    fprintf(stderr, "[miattn] bwd d=%d dq_grid=%lld dkdv_grid=%lld G=%d\n", a.d,
+            (long long)a.B * a.H * p.nqt, (long long)a.B * a.H * p.nkt, p.G);
+  return a.d == 128 ? launch_bwd_d<128>(p, stream) : launch_bwd_d<64>(p, stream);
+}
+
+}  // namespace miattn

@@ -46,6 +46,22 @@ struct DecodeArgs {
   int page_size, max_pages, num_pages;
 };
 
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, H, Hkv, Nq, Nk, d;
+  float scale;
+  int causal, window;
+  void* workspace;
+};
+
 // Query-tile rows / key-tile columns of the bf16 and fp32 forward kernels.
 void fwd_bf16_tile_shape(int d, int* block_m, int* block_n);
 void fwd_f32_tile_shape(int d, int* block_m, int* block_n);
@@ -56,6 +72,11 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 // Partials layout inside the workspace: O_s fp32 [B, H, S, d], then lse_s fp32 [B, H, S].
 size_t decode_workspace_bytes(int B, int H, int d, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+
+// Backward: workspace = D [B, H, Nq] fp32 (256-byte aligned size), then,
+// when H > Hkv, fp32 dK and dV partials [B, H, Nk, d] each.
+size_t bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream);
 
 // Ceiling probes (calib.hip).
 hipError_t launch_mfma_ceiling(int blocks, int iters, float* sink, hipStream_t stream);

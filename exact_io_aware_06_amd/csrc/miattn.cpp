@@ -253,6 +253,38 @@ int attn_fwd_varlen_tile_counts(const void* q, const void* k, const void* v, voi
                         total_k, max_seqlen_q, d, scale, causal, window, counts, stream);
 }
 
+size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
+  if (B < 0 || H < 1 || Hkv < 1 || Nq < 0 || Nk < 0 || d < 1 || H % Hkv != 0) return 0;
+  return miattn::bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d);
+}
+
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv, int B, int H, int Hkv, int Nq,
+             int Nk, int d, float scale, int causal, int window, void* workspace,
+             size_t workspace_bytes, void* stream) {
+  int bm = 0, bn = 0;
+  if (d == 64 || d == 128) miattn::fwd_bf16_tile_shape(d, &bm, &bn);
+  else bm = 1;
+  int st = check_fwd(q, k, v, o, B, H, Hkv, Nq, Nk, d, scale, causal, window, bm);
+  if (st != MIATTN_OK) return st;
+  const long long nq_elems = (long long)B * H * Nq;
+  const long long nk_elems = (long long)B * Hkv * Nk;
+  if (nq_elems > 0 && (dout == nullptr || lse == nullptr || dq == nullptr)) return MIATTN_EINVAL;
+  if (nk_elems > 0 && (dk == nullptr || dv == nullptr)) return MIATTN_EINVAL;
+  if (nk_elems > 0 && (k == nullptr || v == nullptr)) return MIATTN_EINVAL;
+  if (nk_elems > 0 && nq_elems > 0 && q == nullptr) return MIATTN_EINVAL;
+  // the dK / dV kernel's 1-D grid: one work-group per (batch, head, 128 keys)
+  if ((long long)B * H * ((Nk + 127LL) / 128) > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  if ((long long)B * Hkv * Nk * d / 8 / 256 > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  if (B == 0 || (Nq == 0 && Nk == 0)) return MIATTN_OK;
+  const size_t need = miattn::bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d);
+  if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
+  if ((st = device_status()) != MIATTN_OK) return st;
+  miattn::BwdArgs a{q,  k, v, o,     dout,   lse,    dq,       dk,  dv, B, H,
+                    Hkv, Nq, Nk, d, scale, causal, window, workspace};
+  return launch_status(miattn::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 int attn_calib_mfma(int blocks, int iters, float* sink, void* stream) {
   if (blocks < 1 || iters < 1 || sink == nullptr) return MIATTN_EINVAL;
   int st = device_status();

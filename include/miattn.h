@@ -123,6 +123,33 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
                     float scale, int causal, int window, void* stream);
 
 /*
+ * Backward pass of attn_fwd (bf16): the gradients dq, dk, dv of
+ * L = sum(O * dout), recomputing the attention matrix from q, k and the
+ * forward's LSE instead of storing it ("Quadratic Complexity Bottleneck",
+ * FlashAttention entry; "Chapter 3.1 - The Cost of Attention", section 5).
+ * With P = exp(scale q k^T - LSE) over visible pairs and D = rowsum(dout * o):
+ *
+ *     dv = P^T dout,  dS = P * (dout v^T - D),  dq = scale dS k,
+ *     dk = scale dS^T q          (a K/V head sums over its G query heads).
+ *
+ * q, o, dout, dq: [B, H, Nq, d] bf16; k, v, dk, dv: [B, Hkv, Nk, d] bf16;
+ * lse: [B, H, Nq] fp32 as written by attn_fwd for the same q, k, v, scale,
+ * causal and window (rows that see no key have LSE = -inf and get dq = 0;
+ * keys no row sees get dk = dv = 0). Outputs are rounded once to bf16 from
+ * fp32. Every output element is written by exactly one work-item, so
+ * results are deterministic.
+ * workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes
+ * (else MIATTN_EWORKSPACE): D, plus fp32 dk / dv partials per query head
+ * when H > Hkv. Other conventions and errors as for attn_fwd.
+ */
+size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
+int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+             const float* lse, void* dq, void* dk, void* dv,
+             int B, int H, int Hkv, int Nq, int Nk, int d,
+             float scale, int causal, int window,
+             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-K decode: one query token per sequence against a KV cache
  * ("Quadratic Complexity Bottleneck", KV cache entry: past K and V are read
  * from the cache; "Attention Research", section 2: split-K over keys for

@@ -28,11 +28,13 @@ from .attention import _f64, visible_mask
 
 
 def attention_bwd_ref(q, k, v, do, scale: float, causal: bool = False, window: int = 0,
-                      return_terms: bool = False):
+                      return_terms: bool = False, kv_heads=None):
     """(dq [B,H,Nq,d], dk [B,Hkv,Nk,d], dv [B,Hkv,Nk,d]) in float64.
 
     With return_terms, also a dict of per-head fp64 intermediates keyed by
     (b, h): "P", "dS" (each [Nq, Nk]) for error bounds in tests.
+    kv_heads restricts the work to the query heads of the listed K/V heads
+    (the other entries of the results stay 0).
     """
     q64, k64, v64, do64 = _f64(q), _f64(k), _f64(v), _f64(do)
     B, H, Nq, d = q64.shape
@@ -46,8 +48,9 @@ def attention_bwd_ref(q, k, v, do, scale: float, causal: bool = False, window: i
     dk = np.zeros_like(k64)
     dv = np.zeros_like(v64)
     terms = {}
+    heads = range(H) if kv_heads is None else [kh * G + i for kh in kv_heads for i in range(G)]
     for b in range(B):
-        for h in range(H):
+        for h in heads:
             kvh = h // G
             s = np.where(vis, scale * (q64[b, h] @ k64[b, kvh].T), -np.inf)
             m = s.max(axis=1, initial=-np.inf)

@@ -42,7 +42,8 @@ def test_header_declares_expected_entry_points():
     for n in ["attn_fwd", "attn_fwd_f32", "attn_decode_splitk", "attn_decode_workspace_bytes",
               "attn_strerror", "attn_fwd_tile_shape", "attn_fwd_tile_counts",
               "attn_decode_num_splits", "attn_fwd_varlen", "attn_fwd_varlen_tile_counts",
-              "attn_decode_splitk_varlen", "attn_decode_paged"]:
+              "attn_decode_splitk_varlen", "attn_decode_paged", "attn_bwd",
+              "attn_bwd_workspace_bytes"]:
         assert n in names
 
 
@@ -223,6 +224,31 @@ def test_decode_paged_invalid_arguments(lib):
     assert pdec(lib, B=0, table=NULL, lens=NULL, q=NULL, o=NULL, ws=NULL) == OK
 
 
+def bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, B=1,
+        H=4, Hkv=2, Nq=16, Nk=16, d=128, scale=0.1, causal=1, window=0, ws=FAKE,
+        ws_bytes=1 << 30):
+    return lib.attn_bwd(q, k, v, o, do, lse, dq, dk, dv, B, H, Hkv, Nq, Nk, d,
+                        ctypes.c_float(scale), causal, window, ws, ws_bytes, NULL)
+
+
+def test_bwd_invalid_arguments(lib):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: NULL}) == EINVAL, name
+    assert bwd(lib, H=6, Hkv=4) == EINVAL
+    assert bwd(lib, causal=2) == EINVAL
+    assert bwd(lib, window=-1) == EINVAL
+    assert bwd(lib, scale=float("nan")) == EINVAL
+    assert bwd(lib, d=96) == EUNSUP
+    assert bwd(lib, ws=NULL) == EWS
+    assert bwd(lib, ws_bytes=64) == EWS
+    assert bwd(lib, B=0, q=NULL, k=NULL, v=NULL, o=NULL, do=NULL, lse=NULL, dq=NULL, dk=NULL,
+               dv=NULL, ws=NULL) == OK
+    # workspace: D (256-byte aligned), plus fp32 dk/dv partials per query head with GQA
+    assert lib.attn_bwd_workspace_bytes(1, 4, 4, 100, 50, 64) == 1792  # 1600 B rounded to 256
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 100, 50, 64) == 1792 + 2 * 4 * 50 * 64 * 4
+    assert lib.attn_bwd_workspace_bytes(1, 6, 4, 10, 10, 64) == 0
+
+
 def _no_gpu():
     try:
         import torch
@@ -239,3 +265,4 @@ def test_valid_call_without_device_reports_nodevice(lib):
     assert vfwd(lib) == ENODEV
     assert vdec(lib) == ENODEV
     assert pdec(lib) == ENODEV
+    assert bwd(lib) == ENODEV
