@@ -178,7 +178,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens",
-                                       "paged"],
+                                       "paged", "backward"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
@@ -249,6 +249,11 @@ def main():
     pg_table, num_pages = synth.inputs.paged_block_table(0, kv_lens, page_size)
     qg, kpg, vpg = synth.inputs.paged_inputs(cg, num_pages, page_size, seed=0, device=dev)
     pg_table_dev = torch.from_numpy(pg_table).to(dev)
+    # Backward of the headline prefill: the forward's O and LSE, a seeded dO.
+    dout = synth.gen_normal((cp.B, cp.H, cp.Nq, cp.d), 0, 4, 0, "bf16", 1.0, dev)
+    dq_b, dk_b, dv_b = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = torch.empty(mi.bwd_workspace_bytes(cp.B, cp.H, cp.Hkv, cp.Nq, cp.Nk, cp.d),
+                      dtype=torch.uint8, device=dev)
 
     parts = {
         "prefill": lambda: mi.attn_fwd(q, k, v, scale=cp.scale, causal=cp.causal,
@@ -263,13 +268,16 @@ def main():
         "kvlens": lambda: mi.attn_decode_varlen(qd, kc, vc, kv_lens_dev, scale=ck.scale,
                                                 window=ck.window, num_splits=ck.splits,
                                                 out=od, lse=lsed, workspace=ws),
+        "backward": lambda: mi.attn_bwd(q, k, v, o, lse, dout, scale=cp.scale,
+                                        causal=cp.causal, window=cp.window, dq=dq_b, dk=dk_b,
+                                        dv=dv_b, workspace=bws),
         "paged": lambda: mi.attn_decode_paged(qg, kpg, vpg, pg_table_dev, kv_lens_dev,
                                               scale=cg.scale, window=cg.window,
                                               num_splits=cg.splits, out=od, lse=lsed,
                                               workspace=ws),
     }
     core = ["prefill", "decode", "fp32"]
-    ext = [] if args.no_extensions else ["packed", "kvlens", "paged"]
+    ext = [] if args.no_extensions else ["packed", "kvlens", "paged", "backward"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -303,6 +311,9 @@ def main():
         ms = {n: [e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
         return wall, ms
 
+    if "backward" in core:
+        parts["prefill"]()  # O and LSE, inputs of the backward
+        torch.cuda.synchronize()
     wall, ms = timed(core)
     ext_ms = timed(ext)[1] if ext else {}
     ms.update(ext_ms)
@@ -322,13 +333,15 @@ def main():
     kvl_bytes = accounting.decode_kvlens_bytes(ck.H, ck.Hkv, kv_lens, ck.d, window=ck.window)
     pg_bytes = accounting.decode_paged_bytes(cg.H, cg.Hkv, kv_lens, cg.d, page_size,
                                              window=cg.window)
+    bwd_flops = accounting.backward_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
     if args.only != "all":
         xs = ms[args.only]
         val, unit = {"prefill": (pre_tflops, "TFLOP/s"), "decode": (dec_gbs, "GB/s"),
                      "fp32": (rate(f32_flops, mean(f32_ms)) / 1e12, "TFLOP/s"),
                      "packed": (rate(pk_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s"),
-                     "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s")}[args.only]
+                     "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s"),
+                     "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s")}[args.only]
         print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
                           "ms_min": round(min(xs), 4), "value": round(val, 2),
                           "unit": unit, "steps": args.steps}))
@@ -401,6 +414,17 @@ def main():
             "algorithmic_bytes": pg_bytes,
             "ms": round(mean(ms["paged"]), 4), "ms_min": round(min(ms["paged"]), 4),
             "value": round(pg_gbs, 1), "unit": "GB/s", "frac_hbm": round(pg_gbs / PEAK_HBM_GBS, 4)}
+    if "backward" in ms:
+        bw_tf = rate(bwd_flops, mean(ms["backward"])) / 1e12
+        out["backward"] = {
+            "workload": "backward of the causal GQA prefill (B1 H32 Hkv8 N8192 d128, sharpened), "
+                        "seeded N(0,1) dO, O and LSE from the forward",
+            "algorithmic_flops": bwd_flops,
+            "executed_flops": accounting.backward_executed_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d,
+                                                                 cp.causal, cp.window),
+            "ms": round(mean(ms["backward"]), 4), "ms_min": round(min(ms["backward"]), 4),
+            "value": round(bw_tf, 2), "unit": "TFLOP/s",
+            "frac_peak": round(bw_tf / PEAK_BF16_TFLOPS, 4)}
     if ceilings:
         out["roofline"]["frac_of_measured_ceiling"] = round(
             pre_tflops / ceilings["mfma_bf16_tflops"], 4)

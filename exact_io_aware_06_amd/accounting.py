@@ -115,3 +115,15 @@ def decode_paged_bytes(H, Hkv, kv_lens, d, page_size, elem_bytes=2, window=0, ls
     sequence sees, q, O and LSE, plus the block-table entries of its pages."""
     pages = sum(-(-int(n) // page_size) for n in kv_lens)
     return decode_kvlens_bytes(H, Hkv, kv_lens, d, elem_bytes, window, lse) + 4 * pages
+
+
+def backward_flops(B, H, Nq, Nk, d, causal, window) -> int:
+    """Algorithmic FLOPs of one backward call: 10 d per visible pair per head
+    (recomputing S, then dP, dV, dK and dQ at 2 d each: 2.5 x the forward)."""
+    return 10 * d * visible_pairs(Nq, Nk, causal, window) * B * H
+
+
+def backward_executed_flops(B, H, Nq, Nk, d, causal, window) -> int:
+    """Matrix-core FLOPs the two-kernel backward actually issues: S and dP are
+    computed in both the dQ pass and the dK/dV pass, 14 d per visible pair."""
+    return 14 * d * visible_pairs(Nq, Nk, causal, window) * B * H
