@@ -9,6 +9,7 @@ the first call does, and raises if it has not been built.
 from .api import (  # noqa: F401
     MiattnError,
     attn_fwd,
+    attn_fwd_fp8,
     attn_fwd_varlen,
     attn_decode,
     attn_decode_varlen,

@@ -49,6 +49,8 @@ def load_library():
         lib.attn_fwd.restype = I
         lib.attn_fwd_f32.argtypes = fwd_args
         lib.attn_fwd_f32.restype = I
+        lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, F, I, I, P]
+        lib.attn_fwd_fp8.restype = I
         lib.attn_fwd_tile_counts.argtypes = fwd_args[:-1] + [P, P]
         lib.attn_fwd_tile_counts.restype = I
         varlen_args = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I]
@@ -146,6 +148,37 @@ def attn_fwd(q, k, v, scale=None, causal=False, window=0, out=None, lse=None):
     with torch.cuda.device(q.device):
         _check(fn(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv, Nq, Nk, d,
                   ctypes.c_float(scale), int(bool(causal)), int(window), _stream(q.device)))
+    return out, lse
+
+
+def attn_fwd_fp8(q8, k8, v, q_descale, k_descale, scale=None, causal=False, window=0,
+                 out=None, lse=None):
+    """FP8 forward: q8 [B,H,Nq,d], k8 [B,Hkv,Nk,d] float8_e4m3fn with per-tensor
+    descales; v [B,Hkv,Nk,d] bf16. Returns (O bf16 [B,H,Nq,d], LSE fp32 [B,H,Nq])."""
+    import torch
+    _require(q8.dim() == 4 and k8.dim() == 4 and v.dim() == 4, "q8, k8, v must be 4-D")
+    _require(q8.is_cuda and k8.device == q8.device and v.device == q8.device,
+             "q8, k8, v must be on the same GPU")
+    _require(q8.dtype == torch.float8_e4m3fn and k8.dtype == torch.float8_e4m3fn,
+             "q8 and k8 must be float8_e4m3fn")
+    _require(v.dtype == torch.bfloat16, "v must be bfloat16")
+    _require(q8.is_contiguous() and k8.is_contiguous() and v.is_contiguous(),
+             "tensors must be contiguous")
+    B, H, Nq, d = q8.shape
+    Hkv, Nk = k8.shape[1], k8.shape[2]
+    _require(k8.shape[0] == B and k8.shape[3] == d and v.shape == k8.shape,
+             "k8/v must be [B, Hkv, Nk, d] matching q8")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
+    if lse is None:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    lib = load_library()
+    with torch.cuda.device(q8.device):
+        _check(lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv,
+                                Nq, Nk, d, ctypes.c_float(scale), ctypes.c_float(q_descale),
+                                ctypes.c_float(k_descale), int(bool(causal)), int(window),
+                                _stream(q8.device)))
     return out, lse
 
 

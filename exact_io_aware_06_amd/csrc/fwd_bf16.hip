@@ -75,21 +75,28 @@ struct FwdParams {
   const int* cu_k;
 };
 
-template <int D>
+template <int D, bool FP8 = false>
 struct Tile {
   static constexpr int BN = 64;                      // keys per K/V tile
-  static constexpr int ROWB = D * 2;                 // bytes per K/V row
+  static constexpr int ROWB = D * 2;                 // bytes per V row (and bf16 K row)
   static constexpr int CPR = D / 8;                  // 16-byte chunks per row
   static constexpr int RPB = 64 / CPR;               // rows per 1 KB DMA block
-  static constexpr int TILE = BN * ROWB;             // bytes of one K (or V) tile
+  static constexpr int TILE = BN * ROWB;             // bytes of one V (or bf16 K) tile
   static constexpr int NBLK = TILE / 1024;           // DMA blocks per tile and tensor
   static constexpr int BPW = NBLK / 4;               // ... per wave
-  static constexpr int STAGE = 2 * TILE;             // one pipeline stage: K tile, V tile
   static constexpr int KB = BN / 32;                 // 32-key blocks per tile
   static constexpr int DB = D / 32;                  // 32-dim blocks of O
-  static constexpr int KS = D / 16;                  // k-steps of Q K^T
+  static constexpr int KS = D / 16;                  // k-steps of Q K^T (bf16)
   static constexpr int PS = BN / 16;                 // k-steps of P V
-  static_assert(NBLK % 4 == 0, "DMA blocks split over four waves");
+  // K tile: bf16, or fp8 e4m3 (one byte per element) for the fp8 Q K^T.
+  static constexpr int KROWB = FP8 ? D : D * 2;
+  static constexpr int KCPR = KROWB / 16;
+  static constexpr int KRPB = 64 / KCPR;
+  static constexpr int KTILE = BN * KROWB;
+  static constexpr int KBPW = KTILE / 1024 / 4;
+  static constexpr int KS8 = D / 64;                 // k-steps of the fp8 Q K^T
+  static constexpr int LDS = 2 * KTILE + 2 * TILE;   // K ring + V ring
+  static_assert(NBLK % 4 == 0 && (KTILE / 1024) % 4 == 0, "DMA blocks split over four waves");
 };
 
 // LDS layout of a K or V tile: row-major [key][d] with the 16-byte chunks of
@@ -100,6 +107,29 @@ template <int D>
 __device__ __forceinline__ int swz(int r) {
   if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
   return (r >> 1) & 7;
+}
+
+// The same for K rows of KROWB bytes (fp8 K: 128- or 64-byte rows).
+template <int KROWB>
+__device__ __forceinline__ int swzk(int r) {
+  if (KROWB == 256) return ((r & 7) << 1) | ((r >> 3) & 1);
+  if (KROWB == 128) return (r >> 1) & 7;
+  return (r >> 2) & 3;
+}
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// D += A(32x64) * B(64x32), fp8 e4m3 inputs, fp32 accumulate; lane l holds
+// 32 bytes of row l % 32 of A and of column l % 32 of B, for the same
+// 32 values of k (chosen by l / 32); D as for the 32x32x16 products.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  // E8M0 block scales of 2^0 (exponent 127) on both operands
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
+
+__device__ __forceinline__ i32x8 cat_u4(uint4 lo, uint4 hi) {
+  return i32x8{(int)lo.x, (int)lo.y, (int)lo.z, (int)lo.w,
+               (int)hi.x, (int)hi.y, (int)hi.z, (int)hi.w};
 }
 
 __device__ __forceinline__ void decode_workgroup(const FwdParams& p, int id, int& b, int& h,
@@ -126,11 +156,11 @@ __device__ __forceinline__ void decode_workgroup(const FwdParams& p, int id, int
   }
 }
 
-template <int D, bool COUNT>
+template <int D, bool COUNT, bool FP8 = false>
 __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
-  using T = Tile<D>;
+  using T = Tile<D, FP8>;
   constexpr int BN = T::BN;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * T::STAGE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
   lds_u8* const L = lds_ptr(smem);
 
   const int tid = threadIdx.x;
@@ -188,8 +218,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   const long long lo_q = p.window > 0 ? qpos - p.window : 0;
   long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)Nk - 1);
   hi_q = min(hi_q, (long long)Nk - 1);
-  bf16x8 qf[T::KS];
-  {
+  bf16x8 qf[FP8 ? 1 : T::KS];
+  i32x8 qf8[FP8 ? T::KS8 : 1];
+  if constexpr (FP8) {
+    // fp8 rows of D bytes, addressed as uint16 pairs: bytes 64 ks + 32 g .. + 32
+    const uint16_t* qp = p.q + (head_q + (qvalid ? qrow : 0)) * (D / 2) + g * 16;
+#pragma unroll
+    for (int ks = 0; ks < T::KS8; ++ks)
+      qf8[ks] = cat_u4(load16(qp + ks * 32, qvalid), load16(qp + ks * 32 + 8, qvalid));
+  } else {
     const uint16_t* qp = p.q + (head_q + (qvalid ? qrow : 0)) * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qp + ks * 16, qvalid));
@@ -197,12 +234,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // LDS: K ring of two tiles at [0, 2 TILE), V ring of two tiles at
   // [2 TILE, 4 TILE). K runs two tiles ahead of the softmax, V one tile.
-  constexpr int KRING = 0, VRING = 2 * T::TILE;
+  constexpr int KRING = 0, VRING = 2 * T::KTILE;
 
   // Per-lane LDS byte offsets, fixed for the whole kernel.
   // Q K^T operand: row kb*32 + l32, chunk 2 ks + g.
-  uint32_t koff[T::KS];
-  {
+  uint32_t koff[FP8 ? 1 : T::KS];
+  uint32_t koff8[FP8 ? T::KS8 : 1][2];
+  if constexpr (FP8) {
+    // fp8: row kb*32 + l32, chunks 4 ks + 2 g and 4 ks + 2 g + 1
+    const int sw = swzk<T::KROWB>(l32);
+#pragma unroll
+    for (int ks = 0; ks < T::KS8; ++ks)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+        koff8[ks][hh] = (uint32_t)(l32 * T::KROWB + (((4 * ks + 2 * g + hh) ^ sw) << 4));
+  } else {
     const int sw = swz<D>(l32);
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks)
@@ -236,8 +282,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     const int r = blk * T::RPB + lane / T::CPR;
     dvoff[i] = (uint32_t)(r * T::ROWB + (((lane % T::CPR) ^ swz<D>(r)) << 4));
   }
+  // K tiles have their own geometry when K is fp8.
+  uint32_t dkoff[T::KBPW];
+#pragma unroll
+  for (int i = 0; i < T::KBPW; ++i) {
+    const int blk = wave * T::KBPW + i;
+    const int r = blk * T::KRPB + lane / T::KCPR;
+    dkoff[i] = FP8 ? (uint32_t)(r * T::KROWB + (((lane % T::KCPR) ^ swzk<T::KROWB>(r)) << 4))
+                   : dvoff[i];
+  }
 
-  const uint16_t* kbase = p.k + head_kv * D;
+  const uint16_t* kbase = p.k + head_kv * (T::KROWB / 2);  // uint16 units
   const uint16_t* vbase = p.v + head_kv * D;
   int loaded = 0, masked = 0;
 
@@ -248,6 +303,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + k0 * D, bytes);
 #pragma unroll
     for (int i = 0; i < T::BPW; ++i) dma16(rs, L + slot + (wave * T::BPW + i) * 1024, dvoff[i]);
+  };
+  // DMA of one K tile (bf16 or fp8 rows).
+  auto issue_k = [&](int kt, int slot) {
+    const long long k0 = (long long)kt * BN;
+    const uint32_t bytes = k0 < Nk ? (uint32_t)((Nk - k0) * T::KROWB) : 0u;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(kbase + k0 * (T::KROWB / 2), bytes);
+#pragma unroll
+    for (int i = 0; i < T::KBPW; ++i)
+      dma16(rs, L + slot + (wave * T::KBPW + i) * 1024, dkoff[i]);
   };
 
   // Does key tile kt need the per-element mask for any valid row here?
@@ -273,13 +337,25 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   // S^T = K Q^T of the K tile in ring slot kslot.
   auto qk = [&](int kslot, f32x16 (&sacc)[T::KB]) {
-    const lds_u8* kt_lds = L + KRING + kslot * T::TILE;
+    const lds_u8* kt_lds = L + KRING + kslot * T::KTILE;
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb) {
       sacc[kb] = f32x16{};
+      if constexpr (FP8) {
 #pragma unroll
-      for (int ks = 0; ks < T::KS; ++ks)
-        sacc[kb] = mfma32x32x16(lds_b128(kt_lds, koff[ks] + kb * 32 * T::ROWB), qf[ks], sacc[kb]);
+        for (int ks = 0; ks < T::KS8; ++ks) {
+          const uint32_t o = kb * 32 * T::KROWB;
+          const i32x8 a = cat_u4(
+              __builtin_bit_cast(uint4, lds_b128(kt_lds, koff8[ks][0] + o)),
+              __builtin_bit_cast(uint4, lds_b128(kt_lds, koff8[ks][1] + o)));
+          sacc[kb] = mfma32x32x64_fp8(a, qf8[ks], sacc[kb]);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < T::KS; ++ks)
+          sacc[kb] =
+              mfma32x32x16(lds_b128(kt_lds, koff[ks] + kb * 32 * T::ROWB), qf[ks], sacc[kb]);
+      }
     }
   };
 
@@ -337,7 +413,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
                   f32x16 (&s_nxt)[T::KB], bool mask_next) {
     const int kt = kt_lo + t;
     if (t + 2 < ntiles) {
-      issue(kbase, kt + 2, KRING + (1 - kslot_next) * T::TILE);
+      issue_k(kt + 2, KRING + (1 - kslot_next) * T::KTILE);
       if (COUNT) ++loaded;
     }
     if (t + 1 < ntiles) issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
@@ -383,11 +459,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
   f32x16 sA[T::KB], sB[T::KB];
   if (ntiles > 0) {
-    issue(kbase, kt_lo, KRING);
+    issue_k(kt_lo, KRING);
     issue(vbase, kt_lo, VRING);
     if (COUNT) ++loaded;
     if (ntiles > 1) {
-      issue(kbase, kt_lo + 1, KRING + T::TILE);
+      issue_k(kt_lo + 1, KRING + T::KTILE);
       if (COUNT) ++loaded;
     }
     wait_vmem();
@@ -433,11 +509,12 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 }
 
 template <int D>
-hipError_t launch_d(const FwdParams& prm, hipStream_t stream, bool count) {
+hipError_t launch_d(const FwdParams& prm, hipStream_t stream, bool count, bool fp8) {
   const unsigned nblk = (unsigned)((size_t)prm.B * prm.H * prm.nqt);
   void* args[] = {const_cast<FwdParams*>(&prm)};
-  const void* fn = count ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, true>)
-                         : reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false>);
+  const void* fn = fp8     ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false, true>)
+                   : count ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, true>)
+                           : reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false>);
   return hipLaunchKernel(fn, dim3(nblk), dim3(kThreads), args, 0, stream);
 }
 
@@ -475,7 +552,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
     fprintf(stderr, "[miattn] fwd_bf16 d=%d grid=%lld block=%d BM=%d BN=%d xcd_remap=%d\n", a.d,
             (long long)a.B * a.H * p.nqt, kThreads, kBM, Tile<128>::BN, p.xcd_remap);
   const bool count = a.counts != nullptr;
-  return a.d == 128 ? launch_d<128>(p, stream, count) : launch_d<64>(p, stream, count);
+  return a.d == 128 ? launch_d<128>(p, stream, count, a.fp8 != 0)
+                    : launch_d<64>(p, stream, count, a.fp8 != 0);
 }
 
 }  // namespace miattn

@@ -24,6 +24,8 @@ struct FwdArgs {
   const int* cu_q;
   const int* cu_k;
   int max_q;
+  // fp8 e4m3 q and k (the scale already includes both descales); v stays bf16.
+  int fp8;
 };
 
 struct DecodeArgs {

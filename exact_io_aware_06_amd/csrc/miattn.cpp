@@ -177,6 +177,25 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  stream);
 }
 
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse, int B,
+                 int H, int Hkv, int Nq, int Nk, int d, float scale, float q_descale,
+                 float k_descale, int causal, int window, void* stream) {
+  if (!valid_scale(q_descale) || !valid_scale(k_descale)) return MIATTN_EINVAL;
+  const float eff = scale * q_descale * k_descale;
+  if (!valid_scale(scale)) return MIATTN_EINVAL;
+  if (!valid_scale(eff)) return MIATTN_EUNSUPPORTED;  // the product leaves fp32's range
+  int bm = 0, bn = 0;
+  if (d == 64 || d == 128) miattn::fwd_bf16_tile_shape(d, &bm, &bn);
+  else bm = 1;
+  int st = check_fwd(q8, k8, v, o, B, H, Hkv, Nq, Nk, d, eff, causal, window, bm);
+  if (st != MIATTN_OK) return st;
+  if (B == 0 || Nq == 0) return MIATTN_OK;
+  if ((st = device_status()) != MIATTN_OK) return st;
+  FwdArgs a{q8, k8, v, o, lse, B, H, Hkv, Nq, Nk, d, eff, causal, window, nullptr,
+            nullptr, nullptr, 0, 1};
+  return launch_status(miattn::launch_fwd_bf16(a, static_cast<hipStream_t>(stream)));
+}
+
 int attn_fwd_tile_counts(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                          int H, int Hkv, int Nq, int Nk, int d, float scale, int causal,
                          int window, int* counts, void* stream) {

@@ -91,6 +91,26 @@ int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float
                  float scale, int causal, int window, void* stream);
 
 /*
+ * FP8 forward: q and k in FP8 E4M3 (OCP e4m3fn: bias 7, max 448, no
+ * infinities), each with one fp32 descale (the real value of a code is
+ * code * descale); v and o bf16; lse fp32. The scores are
+ * s_ij = scale * q_descale * k_descale * sum_c q8[b,h,i,c] * k8[b,kvh,j,c],
+ * computed on the fp8 matrix cores with fp32 results; everything after the
+ * scores (softmax, P V, output) is exactly as in attn_fwd. FP8 is used only
+ * for the Q K^T product, where the pages place the low-precision gain
+ * ("Chapter 3.1 - The Cost of Attention", section 6: FP8 where the accuracy
+ * cost is negligible; "Attention Research", section 4: the softmax is what
+ * makes low-precision attention harder than a GEMM).
+ * Layout, masks, GQA and errors as for attn_fwd; q_descale and k_descale must
+ * be finite and > 0 (MIATTN_EINVAL), and scale * q_descale * k_descale must
+ * stay a finite, non-zero fp32 value (MIATTN_EUNSUPPORTED).
+ */
+int attn_fwd_fp8(const void* q8, const void* k8, const void* v, void* o, float* lse,
+                 int B, int H, int Hkv, int Nq, int Nk, int d,
+                 float scale, float q_descale, float k_descale,
+                 int causal, int window, void* stream);
+
+/*
  * Packed variable-length documents, bfloat16 in and out, fp32 LSE. Several
  * documents are packed along one token axis; the mask restarts at every
  * document boundary, so no row sees another document ("What Lost, and Why",

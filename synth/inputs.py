@@ -278,3 +278,34 @@ def paged_inputs(cfg: DecodeConfig, num_pages: int, page_size: int, seed: int, d
     k = gen_normal((num_pages, cfg.Hkv, page_size, cfg.d), seed, TID_K, 0, cfg.dtype, 1.0, device)
     v = gen_normal((num_pages, cfg.Hkv, page_size, cfg.d), seed, TID_V, 0, cfg.dtype, 1.0, device)
     return q, k, v
+
+
+# ---------------------------------------------------------------------------
+# FP8 (OCP e4m3fn) inputs with one fp32 descale per tensor.
+
+FP8_MAX = 448.0
+
+
+def quantize_fp8(x: torch.Tensor):
+    """(x8 float8_e4m3fn, descale float) with x ~= x8 * descale.
+
+    descale = amax / 448 in fp32, so the largest |x| maps to the largest
+    finite e4m3fn value; every element is rounded to nearest even once.
+    """
+    amax = float(x.abs().max()) if x.numel() else 0.0
+    descale = float(np.float32(amax / FP8_MAX)) if amax > 0 else 1.0
+    x8 = (x.to(torch.float32) / descale).to(torch.float8_e4m3fn)
+    return x8, descale
+
+
+def fp8_prefill_inputs(cfg: PrefillConfig, seed: int, device="cpu"):
+    """(q8, k8, v, q_descale, k_descale): the prefill config's Q and K drawn as
+    for bf16 (fp32 randn times qk_mult) and quantized per tensor to e4m3fn; V bf16."""
+    qs, ks, vs = [], [], []
+    for b in range(cfg.B):
+        qs.append(gen_normal((cfg.H, cfg.Nq, cfg.d), seed, TID_Q, b, "f32", cfg.qk_mult, device))
+        ks.append(gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_K, b, "f32", cfg.qk_mult, device))
+        vs.append(gen_normal((cfg.Hkv, cfg.Nk, cfg.d), seed, TID_V, b, "bf16", 1.0, device))
+    q8, qd = quantize_fp8(torch.stack(qs))
+    k8, kd = quantize_fp8(torch.stack(ks))
+    return q8, k8, torch.stack(vs), qd, kd

@@ -43,7 +43,7 @@ def test_header_declares_expected_entry_points():
               "attn_strerror", "attn_fwd_tile_shape", "attn_fwd_tile_counts",
               "attn_decode_num_splits", "attn_fwd_varlen", "attn_fwd_varlen_tile_counts",
               "attn_decode_splitk_varlen", "attn_decode_paged", "attn_bwd",
-              "attn_bwd_workspace_bytes"]:
+              "attn_bwd_workspace_bytes", "attn_fwd_fp8"]:
         assert n in names
 
 
@@ -247,6 +247,21 @@ def test_bwd_invalid_arguments(lib):
     assert lib.attn_bwd_workspace_bytes(1, 4, 4, 100, 50, 64) == 1792  # 1600 B rounded to 256
     assert lib.attn_bwd_workspace_bytes(1, 4, 2, 100, 50, 64) == 1792 + 2 * 4 * 50 * 64 * 4
     assert lib.attn_bwd_workspace_bytes(1, 6, 4, 10, 10, 64) == 0
+
+
+def test_fwd_fp8_invalid_arguments(lib):
+    def f8(q=FAKE, scale=0.1, qd=0.01, kd=0.02, d=128, H=4, Hkv=2):
+        return lib.attn_fwd_fp8(q, FAKE, FAKE, FAKE, FAKE, 1, H, Hkv, 16, 16, d,
+                                ctypes.c_float(scale), ctypes.c_float(qd), ctypes.c_float(kd),
+                                1, 0, NULL)
+    assert f8(q=NULL) == EINVAL
+    assert f8(qd=0.0) == EINVAL
+    assert f8(kd=-1.0) == EINVAL
+    assert f8(qd=float("inf")) == EINVAL
+    assert f8(scale=float("nan")) == EINVAL
+    assert f8(scale=1e-30, qd=1e-10, kd=1e-10) == EUNSUP    # product underflows fp32
+    assert f8(H=6, Hkv=4) == EINVAL
+    assert f8(d=96) == EUNSUP
 
 
 def _no_gpu():

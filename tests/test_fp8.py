@@ -1,0 +1,152 @@
+"""FP8 forward (attn_fwd_fp8): HIP path against the oracle on the dequantized
+inputs (q8 * q_descale, k8 * k_descale, v), i.e. against exact attention of
+the values the kernel is given.
+
+Tolerance: the bf16 forward's (O max-abs 2e-2, mean-abs 2e-3; LSE 1e-3),
+plus the error of the fp8 Q K^T product. The fp8 matrix instruction does not
+sum its 64 exact products exactly: on random codes spanning the whole e4m3
+range its result was measured within 1.4e-4 of the sum of |products|, so the
+bound takes eps8 = 2^-12 of sum_c |q_c k_c| (scaled) for every score. A
+score error of at most Delta_i on row i shifts its LSE by at most Delta_i and
+its softmax weights by a factor within exp(+-2 Delta_i), so
+  |dLSE_i| <= 1e-3 + Delta_i,
+  |dO_ic|  <= 2e-2 + (exp(2 Delta_i) - 1) sum_j w_ij |v_jc|,
+  with Delta_i = eps8 * max over visible j of scale_eff * sum_c |q_ic| |k_jc|.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+import exact_io_aware_06_amd as mi
+from helpers import to64
+from synth import inputs as S
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+EPS8 = 2.0 ** -12
+
+
+def make(B, H, Hkv, Nq, Nk, d, seed, mult=1.0, pow2=False):
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(B, H, Nq, d, generator=g) * mult
+    k = torch.randn(B, Hkv, Nk, d, generator=g) * mult
+    v = torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16)
+    q8, qd = S.quantize_fp8(q)
+    k8, kd = S.quantize_fp8(k)
+    if pow2:  # descales that are powers of two: q8 * qd is exact in bf16
+        qd2, kd2 = 2.0 ** math.ceil(math.log2(qd)), 2.0 ** math.ceil(math.log2(kd))
+        q8, k8 = (q / qd2).to(torch.float8_e4m3fn), (k / kd2).to(torch.float8_e4m3fn)
+        qd, kd = qd2, kd2
+    return q8, k8, v, qd, kd
+
+
+def deq(x8, ds):
+    return x8.to(torch.float64) * ds
+
+
+def run(q8, k8, v, qd, kd, scale, causal, window):
+    o, lse = mi.attn_fwd_fp8(q8.to(DEV), k8.to(DEV), v.to(DEV), qd, kd, scale=scale,
+                             causal=causal, window=window)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def check_rows(q8, k8, v, qd, kd, scale, causal, window, o, lse, b, h, rows, label):
+    """Compare rows of (b, h) with the oracle under the fp8 bound."""
+    Hkv, Nq, Nk = k8.shape[1], q8.shape[2], k8.shape[2]
+    G = q8.shape[1] // Hkv
+    qq, kk = deq(q8, qd), deq(k8, kd)
+    o_ref, l_ref = oracle.attention_rows_ref(qq, kk, v, scale, causal, window, b, h, rows)
+    vis = oracle.visible_mask(Nq, Nk, causal, window, rows)
+    mag = scale * (qq[b, h][rows].abs().numpy() @ kk[b, h // G].abs().numpy().T)
+    delta = EPS8 * np.where(vis, mag, 0.0).max(axis=1, initial=0.0)
+    # softmax weights of the rows (exact), for the O bound
+    s = np.where(vis, scale * (qq[b, h][rows].numpy() @ kk[b, h // G].numpy().T), -np.inf)
+    m = s.max(axis=1, initial=-np.inf)
+    w = np.exp(s - np.where(np.isfinite(m), m, 0)[:, None])
+    w = w / np.where(w.sum(axis=1) > 0, w.sum(axis=1), 1)[:, None]
+    wv = w @ np.abs(to64(v)[b, h // G])
+    og = to64(o)[b, h][rows]
+    lg = to64(lse)[b, h][rows]
+    err_o = np.abs(og - o_ref)
+    tol_o = 2e-2 + np.expm1(2 * delta)[:, None] * wv
+    assert np.all(err_o <= tol_o), f"{label}: O err/bound {float((err_o / tol_o).max()):.3f}"
+    assert err_o.mean() <= 2e-3 + float((np.expm1(2 * delta)[:, None] * wv).mean()), label
+    fin = np.isfinite(l_ref)
+    assert np.array_equal(np.isneginf(lg), ~fin), f"{label}: -inf pattern"
+    err_l = np.abs(lg[fin] - l_ref[fin])
+    assert np.all(err_l <= 1e-3 + delta[fin]), f"{label}: LSE err {float(err_l.max()):.2e}"
+    return float(err_o.max()), float(err_l.max(initial=0.0))
+
+
+CASES = [
+    # B, H, Hkv, Nq, Nk, d, causal, window
+    (1, 4, 2, 300, 300, 128, 1, 0),
+    (2, 2, 2, 200, 200, 64, 0, 0),
+    (1, 4, 1, 150, 333, 128, 1, 70),
+    (1, 2, 2, 77, 200, 128, 1, 0),
+    (1, 2, 1, 260, 100, 64, 1, 0),
+    (1, 4, 4, 129, 129, 128, 0, 40),
+]
+
+
+@pytest.mark.parametrize("B,H,Hkv,Nq,Nk,d,causal,window", CASES)
+def test_fp8_parity(B, H, Hkv, Nq, Nk, d, causal, window):
+    q8, k8, v, qd, kd = make(B, H, Hkv, Nq, Nk, d, seed=Nq + d)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse = run(q8, k8, v, qd, kd, scale, causal, window)
+    for b in range(B):
+        for h in range(H):
+            check_rows(q8, k8, v, qd, kd, scale, causal, window, o, lse, b, h,
+                       np.arange(Nq), f"{(B, H, Hkv, Nq, Nk, d, causal, window)} b{b} h{h}")
+
+
+def test_fp8_sharpened():
+    q8, k8, v, qd, kd = make(1, 4, 2, 384, 384, 128, seed=5, mult=3.0 * 128 ** -0.25)
+    o, lse = run(q8, k8, v, qd, kd, 1.0, 1, 0)
+    for h in range(4):
+        check_rows(q8, k8, v, qd, kd, 1.0, 1, 0, o, lse, 0, h, np.arange(384), f"sharp h{h}")
+
+
+def test_fp8_matches_bf16_kernel_on_exact_inputs():
+    """Power-of-two descales make q8 * qd and k8 * kd exact in bf16: the bf16
+    kernel then sees the same values, and the two paths differ only by the fp8
+    instruction's accumulation (and the fp8 path's bf16 P is the same)."""
+    q8, k8, v, qd, kd = make(1, 4, 2, 256, 256, 128, seed=8, pow2=True)
+    o8, l8 = run(q8, k8, v, qd, kd, 0.088, 1, 0)
+    qb = deq(q8, qd).to(torch.bfloat16).to(DEV)
+    kb = deq(k8, kd).to(torch.bfloat16).to(DEV)
+    assert torch.equal(qb.double().cpu(), deq(q8, qd)) and torch.equal(kb.double().cpu(), deq(k8, kd))
+    ob, lb = mi.attn_fwd(qb, kb, v.to(DEV), scale=0.088, causal=True)
+    torch.cuda.synchronize()
+    assert float((l8 - lb).abs().max()) <= 1e-3
+    assert float((o8.float() - ob.float()).abs().max()) <= 2e-2
+
+
+@pytest.mark.parametrize("causal,window", [(1, 0), (1, 50), (0, 0)])
+def test_fp8_zero_queries_count_visible_keys(causal, window):
+    q8, k8, v, qd, kd = make(1, 2, 1, 200, 260, 128, seed=2)
+    q8 = torch.zeros_like(q8)
+    o, lse = run(q8, k8, v, qd, kd, 1.0, causal, window)
+    count = oracle.visible_mask(200, 260, causal, window).sum(axis=1)
+    lg = to64(lse)[0]
+    for h in range(2):
+        got = np.where(np.isneginf(lg[h]), 0, np.rint(np.exp(lg[h])))
+        assert np.array_equal(got.astype(np.int64), count)
+
+
+def test_fp8_workload_causal_gqa_sampled():
+    """The headline prefill shape with fp8 Q and K (per-tensor descales), sampled rows."""
+    c = synth.CONFIGS["c3"]
+    q8, k8, v, qd, kd = S.fp8_prefill_inputs(c, 0)
+    o, lse = run(q8, k8, v, qd, kd, c.scale, c.causal, c.window)
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 4095, 8190, 8191], rng.integers(0, 8192, 12)]))
+    for h in (0, 7, 21, 31):
+        check_rows(q8, k8, v, qd, kd, c.scale, c.causal, c.window, o, lse, 0, h, rows, f"c3 h{h}")
