@@ -11,11 +11,11 @@ the stream the kernels are launched on, around each call inside the timed
 steps.
 
 Beside the step, and timed in a loop of their own over the same number of
-steps, three variants are measured: packed-document prefill (four 8k
-contexts filled with documents of log-uniform length, the mask restarting at
-every document), the decode over the same cache buffers with a random length
-per sequence, and that decode with its keys in 16-key pages scattered over
-one pool.
+steps, five variants are measured: the prefill with Q and K in fp8, packed-
+document prefill (four 8k contexts filled with documents of log-uniform
+length, the mask restarting at every document), the decode over the same cache
+buffers with a random length per sequence, that decode with its keys in
+16-key pages scattered over one pool, and the backward of the prefill.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extensions]
 """
@@ -178,7 +178,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens",
-                                       "paged", "backward"],
+                                       "paged", "backward", "fp8"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
@@ -249,6 +249,10 @@ def main():
     pg_table, num_pages = synth.inputs.paged_block_table(0, kv_lens, page_size)
     qg, kpg, vpg = synth.inputs.paged_inputs(cg, num_pages, page_size, seed=0, device=dev)
     pg_table_dev = torch.from_numpy(pg_table).to(dev)
+    # The headline prefill with Q and K in fp8 e4m3 (per-tensor descales).
+    q8, k8, v8b, q8_ds, k8_ds = synth.inputs.fp8_prefill_inputs(cp, seed=0, device=dev)
+    o8 = torch.empty_like(o)
+    lse8 = torch.empty_like(lse)
     # Backward of the headline prefill: the forward's O and LSE, a seeded dO.
     dout = synth.gen_normal((cp.B, cp.H, cp.Nq, cp.d), 0, 4, 0, "bf16", 1.0, dev)
     dq_b, dk_b, dv_b = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -268,6 +272,8 @@ def main():
         "kvlens": lambda: mi.attn_decode_varlen(qd, kc, vc, kv_lens_dev, scale=ck.scale,
                                                 window=ck.window, num_splits=ck.splits,
                                                 out=od, lse=lsed, workspace=ws),
+        "fp8": lambda: mi.attn_fwd_fp8(q8, k8, v8b, q8_ds, k8_ds, scale=cp.scale,
+                                       causal=cp.causal, window=cp.window, out=o8, lse=lse8),
         "backward": lambda: mi.attn_bwd(q, k, v, o, lse, dout, scale=cp.scale,
                                         causal=cp.causal, window=cp.window, dq=dq_b, dk=dk_b,
                                         dv=dv_b, workspace=bws),
@@ -277,7 +283,7 @@ def main():
                                               workspace=ws),
     }
     core = ["prefill", "decode", "fp32"]
-    ext = [] if args.no_extensions else ["packed", "kvlens", "paged", "backward"]
+    ext = [] if args.no_extensions else ["fp8", "packed", "kvlens", "paged", "backward"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -341,7 +347,8 @@ def main():
                      "packed": (rate(pk_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s"),
                      "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s"),
-                     "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s")}[args.only]
+                     "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s"),
+                     "fp8": (rate(pre_flops, mean(xs)) / 1e12, "TFLOP/s")}[args.only]
         print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
                           "ms_min": round(min(xs), 4), "value": round(val, 2),
                           "unit": unit, "steps": args.steps}))
@@ -414,6 +421,17 @@ def main():
             "algorithmic_bytes": pg_bytes,
             "ms": round(mean(ms["paged"]), 4), "ms_min": round(min(ms["paged"]), 4),
             "value": round(pg_gbs, 1), "unit": "GB/s", "frac_hbm": round(pg_gbs / PEAK_HBM_GBS, 4)}
+    if "fp8" in ms:
+        f8_tf = rate(pre_flops, mean(ms["fp8"])) / 1e12
+        out["fp8_prefill"] = {
+            "workload": "the headline prefill (B1 H32 Hkv8 N8192 d128 causal, sharpened) with Q "
+                        "and K in fp8 e4m3 (one descale per tensor), V bf16",
+            "algorithmic_flops": pre_flops,
+            "ms": round(mean(ms["fp8"]), 4), "ms_min": round(min(ms["fp8"]), 4),
+            "value": round(f8_tf, 2), "unit": "TFLOP/s",
+            "frac_peak_bf16": round(f8_tf / PEAK_BF16_TFLOPS, 4),
+            "note": "Q K^T runs on the fp8 matrix cores (5.0 PFLOP/s dense), P V on bf16 "
+                    "(2.5 PFLOP/s); half the FLOPs at each rate gives a 3.33 PFLOP/s ceiling"}
     if "backward" in ms:
         bw_tf = rate(bwd_flops, mean(ms["backward"])) / 1e12
         out["backward"] = {
