@@ -15,6 +15,7 @@ from .api import (  # noqa: F401
     attn_decode_varlen,
     attn_decode_paged,
     attn_bwd,
+    attn_bwd_varlen,
     bwd_workspace_bytes,
     decode_workspace_bytes,
     fwd_tile_counts,

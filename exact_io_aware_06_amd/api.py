@@ -68,6 +68,9 @@ def load_library():
         lib.attn_bwd_workspace_bytes.restype = S
         lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, S, P]
         lib.attn_bwd.restype = I
+        lib.attn_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                        F, I, I, P, S, P]
+        lib.attn_bwd_varlen.restype = I
         lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
         lib.attn_fwd_tile_shape.restype = I
         lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
@@ -434,6 +437,42 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, window=0, dq=None,
                             _ptr(dk), _ptr(dv), B, H, Hkv, Nq, Nk, d, ctypes.c_float(scale),
                             int(bool(causal)), int(window), _ptr(workspace),
                             ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+    return dq, dk, dv
+
+
+def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q,
+                    max_seqlen_k, scale=None, causal=False, window=0, dq=None, dk=None, dv=None,
+                    workspace=None):
+    """Backward of attn_fwd_varlen: returns (dq like q, dk like k, dv like v).
+
+    q, o, dout [H, total_q, d] bf16; k, v [Hkv, total_k, d] bf16; lse
+    [H, total_q] fp32 from attn_fwd_varlen with the same arguments.
+    """
+    import torch
+    H, Hkv, total_q, total_k, d, ns = _varlen_checks(q, k, v, cu_seqlens_q, cu_seqlens_k)
+    for t, name in ((o, "o"), (dout, "dout")):
+        _require(t.shape == q.shape and t.dtype == q.dtype and t.device == q.device
+                 and t.is_contiguous(), f"{name} must match q")
+    _require(lse.shape == (H, total_q) and lse.dtype == torch.float32 and lse.device == q.device
+             and lse.is_contiguous(), "lse must be fp32 [H, total_q]")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
+        _require(t.shape == ref.shape and t.dtype == ref.dtype and t.is_contiguous(), f"bad {name}")
+    lib = load_library()
+    nbytes = int(lib.attn_bwd_workspace_bytes(1, H, Hkv, total_q, total_k, d))
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    with torch.cuda.device(q.device):
+        _check(lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                                   _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q),
+                                   _ptr(cu_seqlens_k), ns, H, Hkv, total_q, total_k,
+                                   int(max_seqlen_q), int(max_seqlen_k), d,
+                                   ctypes.c_float(scale), int(bool(causal)), int(window),
+                                   _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                   _stream(q.device)))
     return dq, dk, dv
 
 

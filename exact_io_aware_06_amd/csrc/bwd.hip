@@ -28,6 +28,10 @@
 // Splitting dK/dV work by query head keeps the causal work per work-group
 // balanced enough (heaviest key tiles first) with no cross-work-group
 // reduction other than the small group sum.
+//
+// Packed documents (the backward of the packed forward): the batch index is
+// the document, whose rows are located through the row offsets; work-groups
+// past a document's end exit at once, as in the forward.
 
 #include <cstdio>
 
@@ -135,7 +139,42 @@ struct BwdParams {
   int causal, window;
   int nqt, nkt;
   int xcd_remap;
+  // Packed documents (null for fixed-length calls): B documents whose query
+  // and key rows are [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]) of packed
+  // sequences of Nq and Nk rows.
+  const int* cu_q;
+  const int* cu_k;
 };
+
+// The rows one (batch or document, query head) works on: Nq queries from row
+// head_q of Q / dO / dQ / LSE / D, Nk keys from row head_kv of K / V / dK /
+// dV, and the fp32 dK / dV partials of this query head from row head_p. A
+// document whose offsets are out of order or out of range has no rows.
+struct Rows {
+  int Nq, Nk;
+  size_t head_q, head_kv, head_p;
+};
+
+__device__ __forceinline__ Rows rows_of(const BwdParams& p, int b, int h, int kvh) {
+  Rows r;
+  if (p.cu_q == nullptr) {
+    r.Nq = p.Nq;
+    r.Nk = p.Nk;
+    r.head_q = (size_t)(b * p.H + h) * p.Nq;
+    r.head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
+    r.head_p = (size_t)(b * p.H + h) * p.Nk;
+  } else {
+    const int qs = p.cu_q[b], qe = p.cu_q[b + 1];
+    const int ks = p.cu_k[b], ke = p.cu_k[b + 1];
+    const bool ok = 0 <= qs && qs <= qe && qe <= p.Nq && 0 <= ks && ks <= ke && ke <= p.Nk;
+    r.Nq = ok ? qe - qs : 0;
+    r.Nk = ok ? ke - ks : 0;
+    r.head_q = (size_t)h * p.Nq + (ok ? qs : 0);
+    r.head_kv = (size_t)kvh * p.Nk + (ok ? ks : 0);
+    r.head_p = (size_t)h * p.Nk + (ok ? ks : 0);
+  }
+  return r;
+}
 
 // ---------------------------------------------------------------------------
 // D = rowsum(dO * O), fp32, over the stored (bf16) O.
@@ -197,11 +236,14 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     }
   }
   const int kvh = h / p.G;
+  const Rows R = rows_of(p, b, h, kvh);
+  const int Nq = R.Nq, Nk = R.Nk;
   const int q0 = qt * 128;
-  const int off = p.Nk - p.Nq;
-  const int q_last = min(q0 + 128, p.Nq) - 1;
+  if (q0 >= Nq) return;  // a query tile past the end of its document
+  const int off = Nk - Nq;
+  const int q_last = min(q0 + 128, Nq) - 1;
   const long long p_lo = (long long)q0 + off, p_hi = (long long)q_last + off;
-  long long key_lo = 0, key_hi = p.Nk;
+  long long key_lo = 0, key_hi = Nk;
   if (p.causal) key_hi = min(key_hi, p_hi + 1);
   else if (p.window > 0) key_hi = min(key_hi, p_hi + p.window + 1);
   if (p.window > 0) key_lo = max(key_lo, p_lo - p.window);
@@ -210,12 +252,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const int ntiles = kt_hi - kt_lo;
 
   const int qrow = q0 + wave * 32 + l32;
-  const bool qvalid = qrow < p.Nq;
+  const bool qvalid = qrow < Nq;
   const long long qpos = (long long)qrow + off;
   const long long lo_q = p.window > 0 ? qpos - p.window : 0;
-  long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)p.Nk - 1);
-  hi_q = min(hi_q, (long long)p.Nk - 1);
-  const size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+  long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)Nk - 1);
+  hi_q = min(hi_q, (long long)Nk - 1);
+  const size_t head_q = R.head_q;
 
   bf16x8 qf[KS], df[KS];
   {
@@ -238,13 +280,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < KT::BPW; ++i) doff[i] = dma_off<D, 64>(wave, lane, i);
 
-  const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
+  const size_t head_kv = R.head_kv;
   const uint16_t* kbase = p.k + head_kv * D;
   const uint16_t* vbase = p.v + head_kv * D;
 
   auto tile_partial = [&](int kt) -> bool {
     const long long k0 = (long long)kt * BN, k1 = k0 + BN - 1;
-    if (k1 >= p.Nk) return true;
+    if (k1 >= Nk) return true;
     if (p.causal && k1 > p_lo) return true;
     if (p.window > 0) {
       if (k0 < p_hi - p.window) return true;
@@ -258,8 +300,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
   if (ntiles > 0) {
-    dma_rows<D, 64>(kbase, (long long)kt_lo * BN, p.Nk, L + KRING, doff, wave);
-    dma_rows<D, 64>(vbase, (long long)kt_lo * BN, p.Nk, L + VRING, doff, wave);
+    dma_rows<D, 64>(kbase, (long long)kt_lo * BN, Nk, L + KRING, doff, wave);
+    dma_rows<D, 64>(vbase, (long long)kt_lo * BN, Nk, L + VRING, doff, wave);
     wait_vmem();
     __syncthreads();
   }
@@ -267,9 +309,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     const int kt = kt_lo + t;
     const int slot = t & 1;
     if (t + 1 < ntiles) {
-      dma_rows<D, 64>(kbase, (long long)(kt + 1) * BN, p.Nk, L + KRING + (1 - slot) * KT::BYTES,
+      dma_rows<D, 64>(kbase, (long long)(kt + 1) * BN, Nk, L + KRING + (1 - slot) * KT::BYTES,
                       doff, wave);
-      dma_rows<D, 64>(vbase, (long long)(kt + 1) * BN, p.Nk, L + VRING + (1 - slot) * KT::BYTES,
+      dma_rows<D, 64>(vbase, (long long)(kt + 1) * BN, Nk, L + VRING + (1 - slot) * KT::BYTES,
                       doff, wave);
     }
     const lds_u8* kt_lds = L + KRING + slot * KT::BYTES;
@@ -389,12 +431,15 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
     }
   }
   const int kvh = h / p.G;
+  const Rows R = rows_of(p, b, h, kvh);
+  const int Nq = R.Nq, Nk = R.Nk;
   const int k0 = kt * 128;
-  const int k1 = min(k0 + 127, p.Nk - 1);
-  const int off = p.Nk - p.Nq;
+  if (k0 >= Nk) return;  // a key tile past the end of its document
+  const int k1 = min(k0 + 127, Nk - 1);
+  const int off = Nk - Nq;
 
   // Query rows that see any key of [k0, k1]; steps of 32 rows over them.
-  long long i_lo = 0, i_hi = (long long)p.Nq - 1;
+  long long i_lo = 0, i_hi = (long long)Nq - 1;
   if (p.causal) {
     i_lo = (long long)k0 - off;
     if (p.window > 0) i_hi = min(i_hi, (long long)k1 + p.window - off);
@@ -408,8 +453,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
 
   // This lane's key and the query rows that see it: [jq_lo, jq_hi].
   const int key = k0 + wave * 32 + l32;
-  const bool kvalid = key < p.Nk;
-  long long jq_lo = 0, jq_hi = (long long)p.Nq - 1;
+  const bool kvalid = key < Nk;
+  long long jq_lo = 0, jq_hi = (long long)Nq - 1;
   if (p.causal) {
     jq_lo = (long long)key - off;
     if (p.window > 0) jq_hi = (long long)key + p.window - off;
@@ -418,8 +463,8 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
     jq_hi = (long long)key + p.window - off;
   }
 
-  const size_t head_kv = (size_t)(b * p.Hkv + kvh) * p.Nk;
-  const size_t head_q = (size_t)(b * p.H + h) * p.Nq;
+  const size_t head_kv = R.head_kv;
+  const size_t head_q = R.head_q;
   // K as the B operand of S = Q K^T (k = dims), kept in registers.
   bf16x8 kf[KS];
   {
@@ -442,7 +487,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   // exp2-domain LSE and D of query row r (rows past Nq or seeing no key:
   // +inf, so every P of the row is 0).
   auto row_stats = [&](int r, float& l2, float& dl) {
-    const bool ok = r < p.Nq;
+    const bool ok = r < Nq;
     const float l = ok ? p.lse[head_q + r] : -kInf;
     l2 = l == -kInf ? kInf : l * kLog2e;
     dl = ok ? p.delta[head_q + r] : 0.f;
@@ -467,9 +512,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (nsteps > 0) {
-    dma_rows<D, 128>(p.v + head_kv * D, k0, p.Nk, L + VOFF, vdoff, wave);
-    dma_rows<D, 32>(qbase, (long long)st_lo * 32, p.Nq, L + QRING, qdoff, wave);
-    dma_rows<D, 32>(dbase, (long long)st_lo * 32, p.Nq, L + DRING, qdoff, wave);
+    dma_rows<D, 128>(p.v + head_kv * D, k0, Nk, L + VOFF, vdoff, wave);
+    dma_rows<D, 32>(qbase, (long long)st_lo * 32, Nq, L + QRING, qdoff, wave);
+    dma_rows<D, 32>(dbase, (long long)st_lo * 32, Nq, L + DRING, qdoff, wave);
     if (tid < 32) row_stats(st_lo * 32 + tid, stat[0][0][tid], stat[0][1][tid]);
     wait_vmem();
     __syncthreads();
@@ -479,9 +524,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int st = st_lo + t;
     const int slot = t & 1;
     if (t + 1 < nsteps) {
-      dma_rows<D, 32>(qbase, (long long)(st + 1) * 32, p.Nq, L + QRING + (1 - slot) * QT::BYTES,
+      dma_rows<D, 32>(qbase, (long long)(st + 1) * 32, Nq, L + QRING + (1 - slot) * QT::BYTES,
                       qdoff, wave);
-      dma_rows<D, 32>(dbase, (long long)(st + 1) * 32, p.Nq, L + DRING + (1 - slot) * QT::BYTES,
+      dma_rows<D, 32>(dbase, (long long)(st + 1) * 32, Nq, L + DRING + (1 - slot) * QT::BYTES,
                       qdoff, wave);
       if (tid < 32) row_stats((st + 1) * 32 + tid, nl2, ndl);
     }
@@ -572,7 +617,7 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
           *reinterpret_cast<uint2*>(vp + db * 32 + rr * 8) = wv;
         }
     } else {
-      const size_t part = ((size_t)(b * p.H + h) * p.Nk + key) * D + 4 * g;
+      const size_t part = (R.head_p + key) * D + 4 * g;
       float* kp = p.dk_part + part;
       float* vp = p.dv_part + part;
 #pragma unroll
@@ -631,7 +676,9 @@ template <int D>
 hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
   void* args[] = {&prm};
   hipError_t e = hipSuccess;
-  const long long rows = (long long)prm.B * prm.H * prm.Nq;
+  // packed documents share one token axis per head: rows = H * total
+  const long long nb = prm.cu_q != nullptr ? 1 : prm.B;
+  const long long rows = nb * prm.H * prm.Nq;
   if (rows > 0) {
     constexpr int RPB = kThreads / (D / 8);
     void* pargs[] = {&prm, const_cast<long long*>(&rows)};
@@ -650,7 +697,7 @@ hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
   e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>), dim3((unsigned)nkv),
                       dim3(kThreads), args, 0, stream);
   if (e != hipSuccess || prm.G == 1) return e;
-  long long n8 = (long long)prm.B * prm.Hkv * prm.Nk * D / 8;
+  long long n8 = nb * prm.Hkv * prm.Nk * D / 8;
   int d = D;
   void* gargs[] = {&prm, &d, &n8};
   return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gsum_kernel),
@@ -678,10 +725,13 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.dk = static_cast<uint16_t*>(a.dk);
   p.dv = static_cast<uint16_t*>(a.dv);
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  const size_t delta = ((size_t)a.B * a.H * a.Nq * sizeof(float) + 255) / 256 * 256;
+  const size_t nb = a.cu_q != nullptr ? 1 : (size_t)a.B;  // packed: one token axis
+  const size_t delta = (nb * a.H * a.Nq * sizeof(float) + 255) / 256 * 256;
   p.delta = reinterpret_cast<float*>(ws);
   p.dk_part = reinterpret_cast<float*>(ws + delta);
-  p.dv_part = p.dk_part + (size_t)a.B * a.H * a.Nk * a.d;
+  p.dv_part = p.dk_part + nb * a.H * a.Nk * a.d;
+  p.cu_q = a.cu_q;
+  p.cu_k = a.cu_k;
   p.B = a.B;
   p.H = a.H;
   p.Hkv = a.Hkv;
@@ -692,8 +742,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.scale_log2 = a.scale * kLog2e;
   p.causal = a.causal;
   p.window = a.window;
-  p.nqt = (a.Nq + 127) / 128;
-  p.nkt = (a.Nk + 127) / 128;
+  p.nqt = ((a.cu_q != nullptr ? a.max_q : a.Nq) + 127) / 128;
+  p.nkt = ((a.cu_q != nullptr ? a.max_k : a.Nk) + 127) / 128;
   p.xcd_remap = ((a.B * a.Hkv) % 8 == 0) ? 1 : 0;
   if (log_enabled())
     fprintf(stderr, "[miattn] bwd d=%d dq_grid=%lld dkdv_grid=%lld G=%d\n", a.d,

@@ -62,6 +62,11 @@ struct BwdArgs {
   float scale;
   int causal, window;
   void* workspace;
+  // Packed documents (null for fixed-length calls): as FwdArgs; max_q / max_k
+  // bound every document's query / key count. Nq, Nk are the packed totals.
+  const int* cu_q;
+  const int* cu_k;
+  int max_q, max_k;
 };
 
 // Query-tile rows / key-tile columns of the bf16 and fp32 forward kernels.

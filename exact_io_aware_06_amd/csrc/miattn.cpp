@@ -304,6 +304,44 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   return launch_status(miattn::launch_bwd(a, static_cast<hipStream_t>(stream)));
 }
 
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs, int H,
+                    int Hkv, int total_q, int total_k, int max_seqlen_q, int max_seqlen_k,
+                    int d, float scale, int causal, int window, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  if (num_seqs < 0 || H < 1 || Hkv < 1 || total_q < 0 || total_k < 0 || max_seqlen_q < 0 ||
+      max_seqlen_k < 0)
+    return MIATTN_EINVAL;
+  if (H % Hkv != 0) return MIATTN_EINVAL;
+  if (causal != 0 && causal != 1) return MIATTN_EINVAL;
+  if (window < 0 || !valid_scale(scale)) return MIATTN_EINVAL;
+  if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
+  if (num_seqs > 0 && (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)) return MIATTN_EINVAL;
+  if (total_q > 0 && (q == nullptr || o == nullptr || dout == nullptr || lse == nullptr ||
+                      dq == nullptr))
+    return MIATTN_EINVAL;
+  if (total_k > 0 && (k == nullptr || v == nullptr || dk == nullptr || dv == nullptr))
+    return MIATTN_EINVAL;
+  const long long nqt = (max_seqlen_q + 127LL) / 128, nkt = (max_seqlen_k + 127LL) / 128;
+  if ((long long)num_seqs * H * nqt > (long long)INT_MAX ||
+      (long long)num_seqs * H * nkt > (long long)INT_MAX)
+    return MIATTN_EUNSUPPORTED;
+  if ((long long)total_k * d * 4 > 0xFFFFFFFFLL ||
+      (long long)Hkv * total_k * d / 8 / 256 > (long long)INT_MAX)
+    return MIATTN_EUNSUPPORTED;
+  if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return MIATTN_OK;
+  const size_t need = miattn::bwd_workspace_bytes(1, H, Hkv, total_q, total_k, d);
+  if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
+  int st = device_status();
+  if (st != MIATTN_OK) return st;
+  miattn::BwdArgs a{q,         k,        v,        o,      dout,   lse,       dq,
+                    dk,        dv,       num_seqs, H,      Hkv,    total_q,   total_k,
+                    d,         scale,    causal,   window, workspace, cu_seqlens_q,
+                    cu_seqlens_k, max_seqlen_q, max_seqlen_k};
+  return launch_status(miattn::launch_bwd(a, static_cast<hipStream_t>(stream)));
+}
+
 int attn_calib_mfma(int blocks, int iters, float* sink, void* stream) {
   if (blocks < 1 || iters < 1 || sink == nullptr) return MIATTN_EINVAL;
   int st = device_status();

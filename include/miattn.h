@@ -170,6 +170,27 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
              void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Backward of attn_fwd_varlen (packed documents): dq, dk, dv of the packed
+ * forward, each document's gradients depending only on its own rows.
+ * Layout as attn_fwd_varlen: q, o, dout, dq [H, total_q, d] bf16; k, v, dk, dv
+ * [Hkv, total_k, d] bf16; lse [H, total_q] fp32 as written by attn_fwd_varlen
+ * for the same arguments; cu_seqlens_* device int32 [num_seqs + 1].
+ * max_seqlen_q / max_seqlen_k: host-side bounds of every document's query /
+ * key count (they size the grids). Key rows of a document with no queries get
+ * dk = dv = 0. workspace: attn_bwd_workspace_bytes(1, H, Hkv, total_q,
+ * total_k, d) bytes. A document with bad offsets is skipped, as in
+ * attn_fwd_varlen: its dq rows are not written and, when H > Hkv, its dk / dv
+ * rows are unspecified. Other conventions as for attn_bwd.
+ */
+int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
+                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                    const int* cu_seqlens_q, const int* cu_seqlens_k, int num_seqs,
+                    int H, int Hkv, int total_q, int total_k,
+                    int max_seqlen_q, int max_seqlen_k, int d,
+                    float scale, int causal, int window,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Split-K decode: one query token per sequence against a KV cache
  * ("Quadratic Complexity Bottleneck", KV cache entry: past K and V are read
  * from the cache; "Attention Research", section 2: split-K over keys for

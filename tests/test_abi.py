@@ -43,7 +43,7 @@ def test_header_declares_expected_entry_points():
               "attn_strerror", "attn_fwd_tile_shape", "attn_fwd_tile_counts",
               "attn_decode_num_splits", "attn_fwd_varlen", "attn_fwd_varlen_tile_counts",
               "attn_decode_splitk_varlen", "attn_decode_paged", "attn_bwd",
-              "attn_bwd_workspace_bytes", "attn_fwd_fp8"]:
+              "attn_bwd_workspace_bytes", "attn_fwd_fp8", "attn_bwd_varlen"]:
         assert n in names
 
 
@@ -262,6 +262,21 @@ def test_fwd_fp8_invalid_arguments(lib):
     assert f8(scale=1e-30, qd=1e-10, kd=1e-10) == EUNSUP    # product underflows fp32
     assert f8(H=6, Hkv=4) == EINVAL
     assert f8(d=96) == EUNSUP
+
+
+def test_bwd_varlen_invalid_arguments(lib):
+    def bv(cu=FAKE, ns=3, maxq=20, maxk=20, ws_bytes=1 << 30, dq=FAKE, d=128, H=4, Hkv=2):
+        return lib.attn_bwd_varlen(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, cu, cu, ns,
+                                   H, Hkv, 40, 40, maxq, maxk, d, ctypes.c_float(0.1), 1, 0,
+                                   FAKE, ws_bytes, NULL)
+    assert bv(cu=NULL) == EINVAL
+    assert bv(ns=-1) == EINVAL
+    assert bv(maxq=-1) == EINVAL
+    assert bv(dq=NULL) == EINVAL
+    assert bv(H=6, Hkv=4) == EINVAL
+    assert bv(d=80) == EUNSUP
+    assert bv(ws_bytes=16) == EWS
+    assert bv(ns=0, cu=NULL) == OK
 
 
 def _no_gpu():
