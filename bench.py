@@ -178,7 +178,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens",
-                                       "paged", "backward", "fp8"],
+                                       "paged", "backward", "fp8", "packed_backward"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
@@ -240,6 +240,11 @@ def main():
     cu_dev = torch.from_numpy(pk_cu).to(dev)
     op = torch.empty_like(qp)
     lsep = torch.empty(cpk.H, pk_total, dtype=torch.float32, device=dev)
+    # the packed backward: the packed forward's O and LSE, a seeded dO
+    dout_p = synth.gen_normal((cpk.H, pk_total, cpk.d), 0, 4, 0, "bf16", 1.0, dev)
+    dqp, dkp, dvp = torch.empty_like(qp), torch.empty_like(kp), torch.empty_like(vp)
+    bws_p = torch.empty(mi.bwd_workspace_bytes(1, cpk.H, cpk.Hkv, pk_total, pk_total, cpk.d),
+                        dtype=torch.uint8, device=dev)
     ck = synth.inputs.DECODE_KVLENS
     kv_lens = synth.inputs.kv_lengths(0, ck.B, ck.Nk)
     kv_lens_dev = torch.from_numpy(kv_lens).to(dev)
@@ -272,6 +277,10 @@ def main():
         "kvlens": lambda: mi.attn_decode_varlen(qd, kc, vc, kv_lens_dev, scale=ck.scale,
                                                 window=ck.window, num_splits=ck.splits,
                                                 out=od, lse=lsed, workspace=ws),
+        "packed_backward": lambda: mi.attn_bwd_varlen(
+            qp, kp, vp, op, lsep, dout_p, cu_dev, cu_dev, max(pk_lens), max(pk_lens),
+            scale=cpk.scale, causal=cpk.causal, window=cpk.window, dq=dqp, dk=dkp, dv=dvp,
+            workspace=bws_p),
         "fp8": lambda: mi.attn_fwd_fp8(q8, k8, v8b, q8_ds, k8_ds, scale=cp.scale,
                                        causal=cp.causal, window=cp.window, out=o8, lse=lse8),
         "backward": lambda: mi.attn_bwd(q, k, v, o, lse, dout, scale=cp.scale,
@@ -283,7 +292,8 @@ def main():
                                               workspace=ws),
     }
     core = ["prefill", "decode", "fp32"]
-    ext = [] if args.no_extensions else ["fp8", "packed", "kvlens", "paged", "backward"]
+    ext = [] if args.no_extensions else ["fp8", "packed", "packed_backward", "kvlens", "paged",
+                                         "backward"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -319,6 +329,8 @@ def main():
 
     if "backward" in core:
         parts["prefill"]()  # O and LSE, inputs of the backward
+    if "packed_backward" in core:
+        parts["packed"]()
         torch.cuda.synchronize()
     wall, ms = timed(core)
     ext_ms = timed(ext)[1] if ext else {}
@@ -348,7 +360,9 @@ def main():
                      "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s"),
                      "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s"),
                      "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s"),
-                     "fp8": (rate(pre_flops, mean(xs)) / 1e12, "TFLOP/s")}[args.only]
+                     "fp8": (rate(pre_flops, mean(xs)) / 1e12, "TFLOP/s"),
+                     "packed_backward": (rate(2.5 * pk_flops, mean(xs)) / 1e12,
+                                         "TFLOP/s")}[args.only]
         print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
                           "ms_min": round(min(xs), 4), "value": round(val, 2),
                           "unit": unit, "steps": args.steps}))
@@ -432,6 +446,16 @@ def main():
             "frac_peak_bf16": round(f8_tf / PEAK_BF16_TFLOPS, 4),
             "note": "Q K^T runs on the fp8 matrix cores (5.0 PFLOP/s dense), P V on bf16 "
                     "(2.5 PFLOP/s); half the FLOPs at each rate gives a 3.33 PFLOP/s ceiling"}
+    if "packed_backward" in ms:
+        pb_tf = rate(2.5 * pk_flops, mean(ms["packed_backward"])) / 1e12
+        out["packed_backward"] = {
+            "workload": "backward of the packed prefill (24 documents in 4 x 8192 tokens, "
+                        "H32 Hkv8 d128 causal), seeded N(0,1) dO",
+            "algorithmic_flops": int(2.5 * pk_flops),
+            "ms": round(mean(ms["packed_backward"]), 4),
+            "ms_min": round(min(ms["packed_backward"]), 4),
+            "value": round(pb_tf, 2), "unit": "TFLOP/s",
+            "frac_peak": round(pb_tf / PEAK_BF16_TFLOPS, 4)}
     if "backward" in ms:
         bw_tf = rate(bwd_flops, mean(ms["backward"])) / 1e12
         out["backward"] = {
