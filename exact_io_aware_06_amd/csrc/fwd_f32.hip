@@ -8,8 +8,11 @@
 //
 // Each query row is owned by D / 32 consecutive lanes, each holding 32 of its
 // dimensions of q and of the output accumulator; a dot product is a 32-term
-// in-lane sum plus a butterfly over those lanes. Key tiles of 32 rows of K and
-// V sit in LDS; every lane of a row group reads the same K/V row (broadcast).
+// in-lane sum plus a butterfly over those lanes. The four waves of a
+// work-group hold the same query rows and split the key tiles between them
+// (wave w takes tiles w, w + 4, ...), each staging its tiles in its own LDS
+// region; their (max, sum, output) partials are merged once at the end, as
+// the online softmax merges any two partial results.
 
 #include <cstdio>
 
@@ -21,7 +24,7 @@ namespace miattn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBN = 32;
+constexpr int kWaves = kThreads / 64;
 
 struct F32Params {
   const float* q;
@@ -36,20 +39,29 @@ struct F32Params {
 };
 
 template <int D>
+struct F32Tile {
+  static constexpr int TPQ = D / 32;     // lanes per query row
+  static constexpr int BM = 64 / TPQ;    // query rows per work-group (one wave's worth)
+  static constexpr int BN = 2048 / D;    // keys per wave tile (16 KB of K and V per wave)
+};
+
+template <int D>
 __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Params p) {
-  constexpr int TPQ = D / 32;           // lanes per query row
-  constexpr int BM = kThreads / TPQ;    // query rows per work-group
-  __shared__ __attribute__((aligned(16))) float ks[kBN][D];
-  __shared__ __attribute__((aligned(16))) float vs[kBN][D];
+  using T = F32Tile<D>;
+  constexpr int TPQ = T::TPQ, BM = T::BM, BN = T::BN;
+  // per wave: K tile [BN][D] then V tile [BN][D]; reused for the final merge
+  __shared__ __attribute__((aligned(16))) float lds[kWaves][2 * BN * D];
 
   const int tid = threadIdx.x;
-  const int sub = tid % TPQ;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int sub = lane % TPQ;
   const int bh = blockIdx.x / p.nqt;
   const int qt = p.nqt - 1 - (blockIdx.x - bh * p.nqt);
   const int b = bh / p.H, h = bh - b * p.H;
   const int kvh = h / p.G;
   const int q0 = qt * BM;
-  const int qrow = q0 + tid / TPQ;
+  const int qrow = q0 + lane / TPQ;
   const bool qvalid = qrow < p.Nq;
   const int off = p.Nk - p.Nq;
   const long long qpos = (long long)qrow + off;
@@ -70,27 +82,32 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Params p) {
     acc[c] = 0.f;
   }
   float m = -kInf, l = 0.f;
+  float* ks = lds[wave];
+  float* vs = lds[wave] + BN * D;
 
   if (key_hi > key_lo) {
-    const int kt_lo = (int)(key_lo / kBN), kt_hi = (int)((key_hi + kBN - 1) / kBN);
-    for (int kt = kt_lo; kt < kt_hi; ++kt) {
-      const int k0 = kt * kBN;
-      __syncthreads();
-      for (int e = tid; e < kBN * D; e += kThreads) {
+    const int kt_lo = (int)(key_lo / BN), kt_hi = (int)((key_hi + BN - 1) / BN);
+    for (int kt = kt_lo + wave; kt < kt_hi; kt += kWaves) {
+      const int k0 = kt * BN;
+      // this wave's lanes finished reading the previous tile (in-order LDS)
+      __builtin_amdgcn_wave_barrier();
+      for (int e = lane; e < BN * D; e += 64) {
         const int r = e / D, c = e - r * D;
         const bool ok = k0 + r < p.Nk;
-        ks[r][c] = ok ? p.k[(head_kv + k0 + r) * D + c] : 0.f;
-        vs[r][c] = ok ? p.v[(head_kv + k0 + r) * D + c] : 0.f;
+        ks[e] = ok ? p.k[(head_kv + k0 + r) * D + c] : 0.f;
+        vs[e] = ok ? p.v[(head_kv + k0 + r) * D + c] : 0.f;
       }
-      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-      float s[kBN];
+      float s[BN];
       float mx = -kInf;
 #pragma unroll
-      for (int j = 0; j < kBN; ++j) {
+      for (int j = 0; j < BN; ++j) {
         float dot = 0.f;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) dot = __builtin_fmaf(qv[c], ks[j][sub * 32 + c], dot);
+        for (int c = 0; c < 32; ++c) dot = __builtin_fmaf(qv[c], ks[j * D + sub * 32 + c], dot);
 #pragma unroll
         for (int w = 1; w < TPQ; w <<= 1) dot += __shfl_xor(dot, w, 64);
         const long long key = (long long)k0 + j;
@@ -107,28 +124,52 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Params p) {
 #pragma unroll
       for (int c = 0; c < 32; ++c) acc[c] *= alpha;
 #pragma unroll
-      for (int j = 0; j < kBN; ++j) {
+      for (int j = 0; j < BN; ++j) {
         const float e = expf(s[j] - m_new);
         l += e;
 #pragma unroll
-        for (int c = 0; c < 32; ++c) acc[c] = __builtin_fmaf(e, vs[j][sub * 32 + c], acc[c]);
+        for (int c = 0; c < 32; ++c) acc[c] = __builtin_fmaf(e, vs[j * D + sub * 32 + c], acc[c]);
       }
       m = m_new;
     }
   }
 
-  if (qvalid) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
-    for (int c = 0; c < 32; ++c) p.o[(head_q + qrow) * D + sub * 32 + c] = acc[c] * inv;
-    if (sub == 0 && p.lse != nullptr) p.lse[head_q + qrow] = l > 0.f ? m + logf(l) : -kInf;
+  // Merge the four waves' partials: each writes (m, l, acc) to its region,
+  // then wave 0 combines them with weights exp(m_w - M).
+  __syncthreads();
+  {
+    float* mine = lds[wave] + lane * 34;  // 34 floats per lane: m, l, 32 acc
+    mine[0] = m;
+    mine[1] = l;
+    for (int c = 0; c < 32; ++c) mine[2 + c] = acc[c];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    float M = -kInf;
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, lds[w][lane * 34]);
+    float L = 0.f, out[32];
+    for (int c = 0; c < 32; ++c) out[c] = 0.f;
+    if (M != -kInf) {
+      for (int w = 0; w < kWaves; ++w) {
+        const float* part = lds[w] + lane * 34;
+        const float e = part[0] == -kInf ? 0.f : expf(part[0] - M);
+        L += e * part[1];
+        for (int c = 0; c < 32; ++c) out[c] = __builtin_fmaf(e, part[2 + c], out[c]);
+      }
+    }
+    if (qvalid) {
+      const float inv = L > 0.f ? 1.f / L : 0.f;
+      for (int c = 0; c < 32; ++c) p.o[(head_q + qrow) * D + sub * 32 + c] = out[c] * inv;
+      if (sub == 0 && p.lse != nullptr) p.lse[head_q + qrow] = L > 0.f ? M + logf(L) : -kInf;
+    }
   }
 }
 
 }  // namespace
 
 void fwd_f32_tile_shape(int d, int* block_m, int* block_n) {
-  *block_m = kThreads / (d / 32);
-  *block_n = kBN;
+  *block_m = 64 / (d / 32);
+  *block_n = 2048 / d;
 }
 
 hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream) {
