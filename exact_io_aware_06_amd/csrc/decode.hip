@@ -18,9 +18,11 @@
 // through LDS (K as rows, V transposed, as in the prefill kernel); wave w
 // takes keys [32w, 32w + 32) of each tile and treats the G query heads as the
 // 32 columns of a transposed score tile S^T = K Q^T (columns >= G are zero
-// and discarded). Each wave keeps its own running max / sum / output; at the
-// end the four waves are combined through LDS into one normalised partial
-// O_s and its lse_s = ln sum exp(scores) for the chunk.
+// and discarded); a group of more than 32 query heads is split into blocks of
+// 32, one work-group each, which read the same keys. Each wave keeps its own
+// running max / sum / output; at the end the four waves are combined through
+// LDS into one normalised partial O_s and its lse_s = ln sum exp(scores) for
+// the chunk.
 //
 // Merge kernel: per (sequence, query head), LSE = ln sum_s exp(lse_s) and
 // O = sum_s exp(lse_s - LSE) O_s; chunks with no visible key have
@@ -46,6 +48,7 @@ struct SplitParams {
   float* o_s;
   float* lse_s;
   int B, H, Hkv, Nk, G, S;
+  int HB;  // blocks of up to 32 query heads per K/V head (ceil(G / 32))
   int window;
   float scale, scale_log2, thr_raw;
   const int* kv_lens;  // per-sequence key counts, or null (all Nk)
@@ -92,7 +95,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
   const int s = blockIdx.x % p.S;
-  const int bk = blockIdx.x / p.S;
+  const int bhb = blockIdx.x / p.S;
+  const int hb = bhb % p.HB;
+  const int bk = bhb / p.HB;
+  const int g0 = hb * 32;               // first query head of this block in the group
+  const int GB = min(32, p.G - g0);     // query heads in this block
   const int kvh = bk % p.Hkv, b = bk / p.Hkv;
 
   // This sequence's keys (its first n cache rows; the query sits at n - 1),
@@ -106,8 +113,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   const int ntiles = hi > start ? (hi - start + kBN - 1) / kBN : 0;
 
   // Query heads of this group as the B-operand columns.
-  const bool qvalid = l32 < p.G;
-  const int hq = kvh * p.G + (qvalid ? l32 : 0);
+  const bool qvalid = l32 < GB;
+  const int hq = kvh * p.G + g0 + (qvalid ? l32 : 0);
   bf16x8 qf[T::KS];
   {
     const uint16_t* qp = p.q + ((size_t)b * p.H + hq) * D + g * 8;
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < p.G * D; idx += kThreads) {
+  for (int idx = tid; idx < GB * D; idx += kThreads) {
     const int col = idx / D, dim = idx - col * D;
     float M = -kInf;
 #pragma unroll
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
         acc += e * ow[(w * 32 + col) * D + dim];
       }
     }
-    const size_t row = ((size_t)b * p.H + kvh * p.G + col) * p.S + s;
+    const size_t row = ((size_t)b * p.H + kvh * p.G + g0 + col) * p.S + s;
     p.o_s[row * D + dim] = Lb > 0.f ? acc / Lb : 0.f;
     if (dim == 0) p.lse_s[row] = Lf > 0.f ? M * p.scale + fast_log2(Lf) * kLn2 : -kInf;
   }
@@ -353,6 +360,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.Hkv = a.Hkv;
   sp.Nk = a.Nk;
   sp.G = a.H / a.Hkv;
+  sp.HB = (sp.G + 31) / 32;
   sp.S = a.splits;
   sp.window = a.window;
   sp.kv_lens = a.kv_lens;
@@ -364,7 +372,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.scale = a.scale;
   sp.scale_log2 = a.scale * kLog2e;
   sp.thr_raw = kRescaleThreshold / sp.scale_log2;
-  const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * a.splits);
+  const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * sp.HB * a.splits);
   if (log_enabled())
     fprintf(stderr,
             "[miattn] decode d=%d splits=%d kv_lens=%s page_size=%d split_grid=%u "

@@ -142,8 +142,8 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache, const in
   const int S = resolve_splits(B, Hkv, Nk, num_splits);
   if (S < 0) return S;
   if (d != 64 && d != 128) return MIATTN_EUNSUPPORTED;
-  if (H / Hkv > 32) return MIATTN_EUNSUPPORTED;
-  if ((long long)B * Hkv * S > (long long)INT_MAX || (long long)B * H > (long long)INT_MAX)
+  const long long hb = (H / Hkv + 31) / 32;  // blocks of 32 query heads per K/V head
+  if ((long long)B * Hkv * hb * S > (long long)INT_MAX || (long long)B * H > (long long)INT_MAX)
     return MIATTN_EUNSUPPORTED;
   if (B == 0) return MIATTN_OK;
   if (q == nullptr || o == nullptr) return MIATTN_EINVAL;

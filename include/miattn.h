@@ -65,7 +65,7 @@ extern "C" {
 
 #define MIATTN_OK            0
 #define MIATTN_EINVAL       -1 /* bad argument: null pointer, negative size, H % Hkv, ... */
-#define MIATTN_EUNSUPPORTED -2 /* valid but not built: d not 64/128, decode G > 32 */
+#define MIATTN_EUNSUPPORTED -2 /* valid but not built: d not 64/128, sizes past 32-bit grids */
 #define MIATTN_ELAUNCH      -3 /* the HIP runtime refused a launch */
 #define MIATTN_EWORKSPACE   -4 /* decode workspace NULL or smaller than required */
 #define MIATTN_ENODEVICE    -5 /* no HIP device is visible to this process */
@@ -207,7 +207,9 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
  * q, o: [B, H, d] bf16; k_cache, v_cache: [B, Hkv, Nk, d] bf16; lse [B, H]
  * fp32 or NULL. num_splits: 1..Nk, or 0 to let the library choose.
  * workspace: device memory of at least attn_decode_workspace_bytes(...) with
- * the same arguments (else MIATTN_EWORKSPACE). G = H / Hkv must be <= 32.
+ * the same arguments (else MIATTN_EWORKSPACE). Any group size G = H / Hkv:
+ * groups of more than 32 query heads are processed in blocks of 32 (each
+ * block reads the group's keys).
  */
 size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits);
 int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,

@@ -140,7 +140,6 @@ def test_decode_invalid_arguments(lib):
     assert dec(lib, splits=101) == EINVAL
     assert dec(lib, splits=-1) == EINVAL
     assert dec(lib, d=32) == EUNSUP
-    assert dec(lib, H=66, Hkv=1) == EUNSUP     # more than 32 query heads per KV head
     assert dec(lib, ws=NULL) == EWS
     assert dec(lib, ws_bytes=100) == EWS
     assert dec(lib, B=0, q=NULL, k=NULL, v=NULL, o=NULL, ws=NULL) == OK

@@ -40,6 +40,9 @@ CASES = [
     (3, 8, 2, 1000, 64, 7, 0),
     (2, 4, 4, 333, 64, 5, 40),     # G = 1
     (2, 32, 1, 517, 128, 4, 0),    # G = 32 (MQA)
+    (2, 48, 1, 517, 128, 4, 0),    # G = 48: two head blocks, the second half full
+    (1, 64, 1, 300, 64, 3, 30),    # G = 64: two full head blocks
+    (2, 66, 2, 200, 128, 0, 0),    # G = 33: a second block of one head
     (2, 8, 2, 100, 128, 64, 0),    # trailing splits are empty
     (2, 8, 2, 1, 128, 1, 0),       # a single cached key
     (1, 8, 2, 129, 128, 2, 0),

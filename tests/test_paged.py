@@ -63,6 +63,16 @@ def test_paged_parity(ps, d, splits, window):
     check_lse(to64(lse), l_ref, label=label)
 
 
+@pytest.mark.parametrize("H,Hkv", [(48, 1), (80, 2)])
+def test_paged_many_heads_per_group(H, Hkv):
+    """Groups of more than 32 query heads run in blocks of 32 over the same pages."""
+    q, kp, vp, table = paged_case(LENS, 16, H, Hkv, 128, seed=H)
+    o, lse = run_paged(q, kp, vp, table, LENS, 0.088, 0, 4)
+    o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, LENS, 16, 0.088, 0)
+    check_out(to64(o), o_ref, label=f"H={H} Hkv={Hkv}")
+    check_lse(to64(lse), l_ref, label=f"H={H} Hkv={Hkv}")
+
+
 @pytest.mark.parametrize("ps,splits", [(16, 1), (16, 8), (64, 5), (128, 16)])
 def test_paged_matches_contiguous_decode(ps, splits):
     """Same keys, same chunks: identical to the contiguous mixed-length decode."""

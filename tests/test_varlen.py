@@ -245,6 +245,16 @@ def test_decode_varlen_parity(d, splits, window):
     assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("H,Hkv", [(40, 1), (64, 1)])
+def test_decode_varlen_many_heads_per_group(H, Hkv):
+    lens = [0, 1, 200, 333]
+    q, kc, vc = decode_case(len(lens), H, Hkv, 333, 128, seed=H)
+    o, lse = run_decode(q, kc, vc, lens, 0.088, 0, 5)
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.088, 0)
+    check_out(to64(o), o_ref, label=f"H={H}")
+    check_lse(to64(lse), l_ref, label=f"H={H}")
+
+
 def test_decode_varlen_ignores_rows_past_length():
     lens = [3, 700, 1000, 64]
     q, kc, vc = decode_case(4, 8, 2, 1000, 128, seed=2)
