@@ -57,10 +57,15 @@ struct LTile {
   static_assert(NBLK % 4 == 0, "DMA blocks split over four waves");
 };
 
+// The swizzle keeps both kinds of read free of bank conflicts on an LDS that
+// serves 256 bytes (64 banks) per cycle: 16-byte operand reads of 16
+// consecutive rows, and 8-byte transposing reads whose 32 lanes per cycle
+// cover 4 rows (d = 128: the rows of an aligned group of four differ in the
+// high swizzle bits; d = 64: rows r and r + 2 do).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  return (r >> 1) & 7;
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // Per-lane LDS byte offsets into such a tile.

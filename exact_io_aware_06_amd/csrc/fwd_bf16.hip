@@ -100,13 +100,18 @@ struct Tile {
 };
 
 // LDS layout of a K or V tile: row-major [key][d] with the 16-byte chunks of
-// each row permuted by an XOR swizzle, so that 16 lanes reading one chunk of
-// 16 consecutive rows (Q K^T operand) and 16 lanes reading 4 rows x 32 bytes
-// (transposing V^T reads) both hit distinct banks.
+// each row permuted by an XOR swizzle. The LDS serves 256 bytes (64 banks)
+// per cycle: 16 lanes of a 16-byte read, 32 lanes of an 8-byte read. The
+// swizzle keeps both reads free of bank conflicts: the 16 lanes reading one
+// chunk of 16 consecutive rows (Q K^T operand) get 16 different chunk slots,
+// and the 32 lanes of a transposing V^T read (4 rows x 2 chunks x 2 halves,
+// for each of 2 x 2 lane groups) get 64 different banks, because the rows of
+// an aligned group of four differ in the high bits of their swizzle (d = 128;
+// for d = 64, two rows share a 256-byte bank line and rows r, r + 2 differ).
 template <int D>
 __device__ __forceinline__ int swz(int r) {
-  if (D == 128) return ((r & 7) << 1) | ((r >> 3) & 1);
-  return (r >> 1) & 7;
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
 // The same for K rows of KROWB bytes (fp8 K: 128- or 64-byte rows).
