@@ -139,7 +139,7 @@ SWEEP_N = [1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072]
 
 def context_sweep(torch, synth, mi, accounting, dev, steps, warmup):
     """Causal GQA prefill (B1 H32 Hkv8 d128, scale 1/sqrt(d)) over context lengths."""
-    base = synth.CONFIGS["c4"].with_(window=0)
+    base = synth.CONFIGS["window4096_gqa_n32768_d128"].with_(window=0)
     rows = []
     for n in SWEEP_N:
         c = base.with_(name=f"causal{n}", Nq=n, Nk=n)
@@ -192,7 +192,7 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: this library has no multi-GPU path "
               "(each GPU's share of prefill or decode is the single-GPU workload).",
               file=sys.stderr)
         sys.exit(2)
@@ -215,9 +215,9 @@ def main():
                                    "N(0,1) inputs", "unit": "TFLOP/s", "points": rows}))
         return
 
-    cp = synth.CONFIGS["c3"]
-    cd = synth.CONFIGS["c5"]
-    cf = synth.CONFIGS["c1"]
+    cp = synth.CONFIGS["causal_gqa_n8192_d128"]
+    cd = synth.CONFIGS["decode_b64_nk32768_d128"]
+    cf = synth.CONFIGS["f32_n256_d64"]
     q, k, v = synth.prefill_inputs(cp, seed=0, device=dev)
     qd, kc, vc = synth.decode_inputs(cd, seed=0, device=dev)
     qf, kf, vf = synth.prefill_inputs(cf, seed=0, device=dev)
@@ -232,7 +232,7 @@ def main():
 
     # Packed documents (four 8k contexts of log-uniform documents) and decode
     # over the same cache buffers with per-sequence lengths.
-    cpk = synth.inputs.PACKED["p1"]
+    cpk = synth.inputs.PACKED["packed_24docs_4x8192_d128"]
     pk_lens = cpk.lengths(0)
     pk_cu = synth.inputs.cu_seqlens(pk_lens)
     pk_total = int(pk_cu[-1])

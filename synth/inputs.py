@@ -97,20 +97,20 @@ def _f32(x: float) -> float:
 # The five workloads. Shapes follow the contexts the pages discuss (2k-8k
 # training contexts, 32k documents, KV-cache decode); values are i.i.d. N(0,1).
 CONFIGS = {
-    "c1": PrefillConfig("c1", 1, 1, 1, 256, 256, 64, "f32", 0, 0, _f32(1 / 8),
+    "f32_n256_d64": PrefillConfig("f32_n256_d64", 1, 1, 1, 256, 256, 64, "f32", 0, 0, _f32(1 / 8),
                         note="single head, non-causal, fp32"),
-    "c2": PrefillConfig("c2", 4, 16, 16, 2048, 2048, 64, "bf16", 1, 0, _f32(1 / 8),
+    "causal_b4_h16_n2048_d64": PrefillConfig("causal_b4_h16_n2048_d64", 4, 16, 16, 2048, 2048, 64, "bf16", 1, 0, _f32(1 / 8),
                         note="causal self-attention prefill"),
     # Q and K are each multiplied by 3 * d^-1/4 before the bf16 cast, which folds
     # the 1/sqrt(d) into the inputs and sharpens the logits threefold; the kernel
     # scale is therefore 1.0.
-    "c3": PrefillConfig("c3", 1, 32, 8, 8192, 8192, 128, "bf16", 1, 0, 1.0,
+    "causal_gqa_n8192_d128": PrefillConfig("causal_gqa_n8192_d128", 1, 32, 8, 8192, 8192, 128, "bf16", 1, 0, 1.0,
                         qk_mult=3.0 * 128 ** -0.25,
                         note="causal GQA prefill, sharpened logits"),
-    "c4": PrefillConfig("c4", 1, 32, 8, 32768, 32768, 128, "bf16", 1, 4096,
+    "window4096_gqa_n32768_d128": PrefillConfig("window4096_gqa_n32768_d128", 1, 32, 8, 32768, 32768, 128, "bf16", 1, 4096,
                         _f32(1 / math.sqrt(128)),
                         note="causal sliding-window GQA prefill"),
-    "c5": DecodeConfig("c5", 64, 32, 8, 32768, 128, 16, _f32(1 / math.sqrt(128)),
+    "decode_b64_nk32768_d128": DecodeConfig("decode_b64_nk32768_d128", 64, 32, 8, 32768, 128, 16, _f32(1 / math.sqrt(128)),
                        note="split-K decode over a 32k KV cache"),
 }
 
@@ -227,14 +227,14 @@ class PackedConfig:
 # training contexts) each filled with documents of log-uniform length in
 # [64, 8192], causal, the GQA head shape of the prefill workloads.
 PACKED = {
-    "p1": PackedConfig("p1", 32, 8, 128, 4, 8192, 64, 8192, 1, 0,
+    "packed_24docs_4x8192_d128": PackedConfig("packed_24docs_4x8192_d128", 32, 8, 128, 4, 8192, 64, 8192, 1, 0,
                        _f32(1 / math.sqrt(128)),
                        note="packed causal GQA prefill, 4 x 8k contexts, log-uniform documents"),
 }
 
 # Decode over caches of mixed length: the decode workload's shapes with each
 # sequence holding a uniform random number of keys in [1, 32768].
-DECODE_KVLENS = CONFIGS["c5"].with_(name="k1", note="split-K decode, per-sequence cache lengths")
+DECODE_KVLENS = CONFIGS["decode_b64_nk32768_d128"].with_(name="decode_kvlens_b64_nk32768_d128", note="split-K decode, per-sequence cache lengths")
 
 
 def packed_inputs(cfg: PackedConfig, total_q: int, total_k: int, seed: int, device="cpu"):
@@ -268,7 +268,7 @@ def paged_block_table(seed: int, kv_lens, page_size: int, max_pages: int | None 
 
 # Paged decode: the mixed-length decode workload stored in 16-key pages
 # scattered over one pool.
-PAGED = {"page_size": 16, "decode": CONFIGS["c5"].with_(name="g1",
+PAGED = {"page_size": 16, "decode": CONFIGS["decode_b64_nk32768_d128"].with_(name="decode_paged16_b64_nk32768_d128",
                                                          note="split-K decode over a paged cache")}
 
 

@@ -178,7 +178,7 @@ def test_bwd_empty_key_range():
 def test_bwd_workload_causal_gqa_one_group():
     """The headline prefill shape (B1 H32 Hkv8 N8192 d128, causal, sharpened):
     every output of one K/V group against the oracle (4 query heads)."""
-    c = synth.CONFIGS["c3"]
+    c = synth.CONFIGS["causal_gqa_n8192_d128"]
     q, k, v = synth.prefill_inputs(c, 0)
     g = torch.Generator().manual_seed(123)
     do = torch.randn(q.shape, generator=g).to(torch.bfloat16)

@@ -86,7 +86,7 @@ def test_decode_equals_last_row_of_causal_prefill():
 
 def test_workload_decode_full_size_sampled():
     """B=64 sequences, 32k cached keys, 16 splits; checked on sampled sequences."""
-    c = synth.CONFIGS["c5"]
+    c = synth.CONFIGS["decode_b64_nk32768_d128"]
     q, kc, vc = synth.decode_inputs(c, seed=0, device=DEV)
     o, lse = mi.attn_decode(q, kc, vc, scale=c.scale, num_splits=c.splits)
     torch.cuda.synchronize()

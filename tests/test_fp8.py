@@ -143,7 +143,7 @@ def test_fp8_zero_queries_count_visible_keys(causal, window):
 
 def test_fp8_workload_causal_gqa_sampled():
     """The headline prefill shape with fp8 Q and K (per-tensor descales), sampled rows."""
-    c = synth.CONFIGS["c3"]
+    c = synth.CONFIGS["causal_gqa_n8192_d128"]
     q8, k8, v, qd, kd = S.fp8_prefill_inputs(c, 0)
     o, lse = run(q8, k8, v, qd, kd, c.scale, c.causal, c.window)
     rng = np.random.default_rng(0)

@@ -272,7 +272,7 @@ def test_decode_kvlens_rows_match_full():
 
 
 def test_packed_lengths_fill_contexts():
-    cfg = S.PACKED["p1"]
+    cfg = S.PACKED["packed_24docs_4x8192_d128"]
     lens = cfg.lengths(0)
     assert sum(lens) == cfg.contexts * cfg.context_len
     assert all(1 <= n <= cfg.max_len for n in lens)

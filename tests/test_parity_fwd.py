@@ -106,22 +106,22 @@ def test_lse_may_be_omitted():
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_workload_fp32_single_head(seed):
-    c = synth.CONFIGS["c1"]
+    c = synth.CONFIGS["f32_n256_d64"]
     q, k, v = synth.prefill_inputs(c, seed)
     o, lse = run_gpu(c, q, k, v)
     o_ref, lse_ref = oracle.attention_ref(q, k, v, c.scale, c.causal, c.window)
-    check_out(to64(o), o_ref, bf16=False, label="c1")
-    check_lse(to64(lse), lse_ref, label="c1")
+    check_out(to64(o), o_ref, bf16=False, label="f32_n256_d64")
+    check_lse(to64(lse), lse_ref, label="f32_n256_d64")
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_workload_causal_prefill_d64(seed):
-    c = synth.CONFIGS["c2"]
+    c = synth.CONFIGS["causal_b4_h16_n2048_d64"]
     q, k, v = synth.prefill_inputs(c, seed)
     o, lse = run_gpu(c, q, k, v)
     o_ref, lse_ref = oracle.attention_ref(q, k, v, c.scale, c.causal, c.window)
-    check_out(to64(o), o_ref, bf16=True, label="c2")
-    check_lse(to64(lse), lse_ref, label="c2")
+    check_out(to64(o), o_ref, bf16=True, label="causal_b4_h16_n2048_d64")
+    check_lse(to64(lse), lse_ref, label="causal_b4_h16_n2048_d64")
 
 
 def sample_rows(N, rng, extra=()):
@@ -145,7 +145,7 @@ def check_sampled(c, q, k, v, o, lse, heads, rows_fn, seed):
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
 def test_workload_causal_gqa_sharpened(seed):
-    c = synth.CONFIGS["c3"]
+    c = synth.CONFIGS["causal_gqa_n8192_d128"]
     q, k, v = synth.prefill_inputs(c, seed)
     o, lse = run_gpu(c, q, k, v)
     heads = [0, 3, 4, 13, 22, 31]
@@ -154,7 +154,7 @@ def test_workload_causal_gqa_sharpened(seed):
 
 @pytest.mark.parametrize("seed", [0])
 def test_workload_sliding_window(seed):
-    c = synth.CONFIGS["c4"]
+    c = synth.CONFIGS["window4096_gqa_n32768_d128"]
     q, k, v = synth.prefill_inputs(c, seed)
     o, lse = run_gpu(c, q, k, v)
     heads = [0, 9, 31]
@@ -166,7 +166,7 @@ def test_workload_sliding_window(seed):
 def test_long_context_sampled(N):
     """The context sweep's longest points: causal GQA, B1 H32 Hkv8 d128, on
     sampled rows (each oracle row spans all N keys)."""
-    c = synth.CONFIGS["c4"].with_(name=f"causal{N}", Nq=N, Nk=N, window=0)
+    c = synth.CONFIGS["window4096_gqa_n32768_d128"].with_(name=f"causal{N}", Nq=N, Nk=N, window=0)
     q, k, v = synth.prefill_inputs(c, 0, device=DEV)
     o, lse = mi.attn_fwd(q, k, v, scale=c.scale, causal=c.causal, window=c.window)
     torch.cuda.synchronize()
@@ -176,7 +176,7 @@ def test_long_context_sampled(N):
 
 
 def test_repeated_runs_bit_identical():
-    c = synth.CONFIGS["c3"].with_(H=8, Hkv=2, Nq=2048, Nk=2048)
+    c = synth.CONFIGS["causal_gqa_n8192_d128"].with_(H=8, Hkv=2, Nq=2048, Nk=2048)
     q, k, v = synth.prefill_inputs(c, 5)
     o1, l1 = run_gpu(c, q, k, v)
     o2, l2 = run_gpu(c, q, k, v)

@@ -193,7 +193,7 @@ def test_varlen_rows_past_max_seqlen_are_not_written():
 
 def test_packed_workload_full_size_sampled():
     """Four 8k contexts packed with log-uniform documents, H32 Hkv8 d128 causal."""
-    cfg = S.PACKED["p1"]
+    cfg = S.PACKED["packed_24docs_4x8192_d128"]
     lens = cfg.lengths(0)
     cu = S.cu_seqlens(lens)
     total = int(cu[-1])
