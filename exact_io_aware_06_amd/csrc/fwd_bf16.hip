@@ -460,15 +460,37 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 
     // Block B: O^T += V^T P^T.
     const lds_u8* vt_lds = L + VRING + vslot * T::TILE;
+    auto vread = [&](int db, int tt) -> bf16x8 {
+      const uint2 lo = lds_tr_b64(vt_lds, voff[db][0] + tt * 16 * T::ROWB);
+      const uint2 hi = lds_tr_b64(vt_lds, voff[db][1] + tt * 16 * T::ROWB);
+      return __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    };
+    if constexpr (kInterleave) {
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db)
+      for (int db = 0; db < T::DB; ++db)
 #pragma unroll
-      for (int tt = 0; tt < T::PS; ++tt) {
-        const uint2 lo = lds_tr_b64(vt_lds, voff[db][0] + tt * 16 * T::ROWB);
-        const uint2 hi = lds_tr_b64(vt_lds, voff[db][1] + tt * 16 * T::ROWB);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        oacc[db] = mfma32x32x16(va, pf[tt], oacc[db]);
+        for (int tt = 0; tt < T::PS; ++tt) oacc[db] = mfma32x32x16(vread(db, tt), pf[tt], oacc[db]);
+    } else {
+      // Software-pipelined by key step: the V^T operands of step tt + 1 are
+      // read while the DB independent products of step tt issue, so no
+      // product waits for its own LDS read.
+      bf16x8 va[2][T::DB];
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) va[0][db] = vread(db, 0);
+#pragma unroll
+      for (int tt = 0; tt < T::PS; ++tt)
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          oacc[db] = mfma32x32x16(va[tt & 1][db], pf[tt], oacc[db]);
+          if (tt + 1 < T::PS) va[(tt + 1) & 1][db] = vread(db, tt + 1);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DB, 2);
+#pragma unroll
+      for (int i = 0; i < T::DB * T::PS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 2);
+        if (i < T::DB * (T::PS - 1)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
       }
+    }
     if (!kInterleave && mask_next) {
       if (COUNT) ++masked;
       mask_tile(kt + 1, s_nxt);
