@@ -23,10 +23,13 @@
 // Online softmax (the pages' running max and running denominator, rescaling
 // the partial output when the maximum grows) is done lazily: the reference
 // maximum used for the exponentials is only moved when a row's new maximum
-// exceeds it by more than 2^8 in the exp2 domain. The final O / l and
-// LSE = m + ln l are identical in exact arithmetic for any reference value;
-// bounding the growth keeps P <= 256, far from fp32/bf16 overflow, and skips
-// most of the rescaling multiplies.
+// exceeds it by more than 2^8 in the exp2 domain, and it is then set 2^24
+// above the new maximum. The final O / l and LSE = m + ln l are identical in
+// exact arithmetic for any reference value, and in floating point P keeps its
+// relative precision at any magnitude (only terms below ~2^-100 of the row
+// maximum underflow). Bounding the growth keeps P <= 256, far from fp32/bf16
+// overflow; the headroom lets a row's maximum grow by 2^32 before the partial
+// output has to be rescaled, which skips most of the rescaling multiplies.
 //
 // Packed documents ("What Lost, and Why", closing section: the mask restarts
 // at every document boundary) reuse the same kernel: the batch index becomes
@@ -43,6 +46,7 @@
 // of the work-group are never loaded; only tiles that straddle a mask edge
 // (or the end of the keys) evaluate the mask per element.
 
+#include <cmath>
 #include <cstdio>
 
 #include "common.hpp"
@@ -56,6 +60,8 @@ constexpr int kBM = 128;
 constexpr int kThreads = 256;
 // exp2-domain head-room before the reference maximum is moved.
 constexpr float kRescaleThreshold = 8.0f;
+// exp2-domain headroom above a row's new maximum when the reference moves.
+constexpr float kRescaleHeadroom = 24.0f;
 
 struct FwdParams {
   const uint16_t* q;
@@ -67,6 +73,7 @@ struct FwdParams {
   float scale;       // softmax scale on q.k
   float scale_log2;  // scale * log2(e)
   float thr_raw;     // kRescaleThreshold / scale_log2, in q.k units
+  float head_raw;    // kRescaleHeadroom / scale_log2, in q.k units (0 if not finite)
   int causal, window;
   int nqt;
   int xcd_remap;
@@ -395,8 +402,10 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     const bool need = m_new > m_ref + p.thr_raw;
     if (wave_any(need)) {
       mfma_drain();  // O was last written by matrix-core instructions
-      const float alpha = need ? fast_exp2((m_ref - m_new) * p.scale_log2) : 1.f;
-      if (need) m_ref = m_new;
+      const float m_up = m_new + p.head_raw;
+      const float m_set = __builtin_isfinite(m_up) ? m_up : m_new;
+      const float alpha = need ? fast_exp2((m_ref - m_set) * p.scale_log2) : 1.f;
+      if (need) m_ref = m_set;
       l_b *= alpha;
       l_f *= alpha;
 #pragma unroll
@@ -594,6 +603,8 @@ hipError_t launch_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   p.scale = a.scale;
   p.scale_log2 = a.scale * kLog2e;
   p.thr_raw = kRescaleThreshold / p.scale_log2;
+  p.head_raw = kRescaleHeadroom / p.scale_log2;
+  if (!std::isfinite(p.head_raw)) p.head_raw = 0.f;
   p.causal = a.causal;
   p.window = a.window;
   p.cu_q = a.cu_q;

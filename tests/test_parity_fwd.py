@@ -101,6 +101,25 @@ def test_lse_may_be_omitted():
     assert torch.equal(out, o_ref)
 
 
+@pytest.mark.parametrize("growth", [20.0, 60.0, 200.0])
+@pytest.mark.parametrize("causal", [0, 1])
+def test_rising_scores(growth, causal):
+    """Scores that rise along the keys by `growth` over the row: every row's
+    maximum keeps growing, so the lazily moved reference maximum is moved
+    again and again (from one move per few tiles up to one per tile)."""
+    B, H, Hkv, N, d = 1, 2, 1, 1000, 128
+    g = torch.Generator().manual_seed(int(growth) + causal)
+    ramp = torch.linspace(0.0, 1.0, N)[None, None, :, None]
+    q = (1.0 + 0.1 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
+    k = (ramp * (growth / d) + 0.05 * torch.randn(B, Hkv, N, d, generator=g) / d).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    c = cfg(B, H, Hkv, N, N, d, causal, 0, scale=1.0)
+    o, lse = run_gpu(c, q, k, v)
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, 1.0, causal, 0)
+    check_out(to64(o), o_ref, bf16=True, label=f"growth={growth} causal={causal}")
+    check_lse(to64(lse), lse_ref, label=f"growth={growth} causal={causal}")
+
+
 # ---------------------------------------------------------------- workloads
 
 
