@@ -322,17 +322,35 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     const lds_u8* kt_lds = L + KRING + slot * KT::BYTES;
     const lds_u8* vt_lds = L + VRING + slot * KT::BYTES;
 
-    // S^T = K Q^T and dP^T = V dO^T (keys as rows, this wave's rows as columns).
+    // S^T = K Q^T and dP^T = V dO^T (keys as rows, this wave's rows as columns),
+    // software-pipelined by k-step: the K and V operands of step ks + 1 are
+    // read while the 2 KB independent products of step ks issue.
     f32x16 s[KB], dp[KB];
+    {
+      bf16x8 ka[2][KB], vb[2][KB];
 #pragma unroll
-    for (int kb = 0; kb < KB; ++kb) {
-      s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      for (int kb = 0; kb < KB; ++kb) {
+        s[kb] = f32x16{};
+        dp[kb] = f32x16{};
+        ka[0][kb] = lds_b128(kt_lds, lo.row_off[0] + kb * 32 * KT::ROWB);
+        vb[0][kb] = lds_b128(vt_lds, lo.row_off[0] + kb * 32 * KT::ROWB);
+      }
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        const uint32_t o = lo.row_off[ks] + kb * 32 * KT::ROWB;
-        s[kb] = mfma32x32x16(lds_b128(kt_lds, o), qf[ks], s[kb]);
-        dp[kb] = mfma32x32x16(lds_b128(vt_lds, o), df[ks], dp[kb]);
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb) {
+          s[kb] = mfma32x32x16(ka[ks & 1][kb], qf[ks], s[kb]);
+          if (ks + 1 < KS)
+            ka[(ks + 1) & 1][kb] = lds_b128(kt_lds, lo.row_off[ks + 1] + kb * 32 * KT::ROWB);
+          dp[kb] = mfma32x32x16(vb[ks & 1][kb], df[ks], dp[kb]);
+          if (ks + 1 < KS)
+            vb[(ks + 1) & 1][kb] = lds_b128(vt_lds, lo.row_off[ks + 1] + kb * 32 * KT::ROWB);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * KB, 3);
+#pragma unroll
+      for (int i = 0; i < 2 * KB * KS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 3);
+        if (i < 2 * KB * (KS - 1)) __builtin_amdgcn_sched_group_barrier(0x100, 1, 3);
       }
     }
     mfma_drain();
@@ -365,15 +383,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
         dsf[kb * 2 + hf] = to_bf16x8(ds);
       }
 
-    // dQ^T += K^T dS^T.
+    // dQ^T += K^T dS^T, software-pipelined by key step like the S^T products.
+    {
+      auto kread = [&](int db, int tt) {
+        return tr_operand(kt_lds, lo.tr_off[db][0] + tt * 16 * KT::ROWB,
+                          lo.tr_off[db][1] + tt * 16 * KT::ROWB);
+      };
+      bf16x8 kt_op[2][DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db) kt_op[0][db] = kread(db, 0);
 #pragma unroll
       for (int tt = 0; tt < PS; ++tt)
-        acc[db] = mfma32x32x16(
-            tr_operand(kt_lds, lo.tr_off[db][0] + tt * 16 * KT::ROWB,
-                       lo.tr_off[db][1] + tt * 16 * KT::ROWB),
-            dsf[tt], acc[db]);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+          acc[db] = mfma32x32x16(kt_op[tt & 1][db], dsf[tt], acc[db]);
+          if (tt + 1 < PS) kt_op[(tt + 1) & 1][db] = kread(db, tt + 1);
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * DB, 4);
+#pragma unroll
+      for (int i = 0; i < DB * PS; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 4);
+        if (i < DB * (PS - 1)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 4);
+      }
+    }
 
     wait_vmem();
     __syncthreads();
