@@ -289,16 +289,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const uint16_t* kbase = p.k + head_kv * D;
   const uint16_t* vbase = p.v + head_kv * D;
 
-  auto tile_partial = [&](int kt) -> bool {
-    const long long k0 = (long long)kt * BN, k1 = k0 + BN - 1;
-    if (k1 >= Nk) return true;
-    if (p.causal && k1 > p_lo) return true;
-    if (p.window > 0) {
-      if (k0 < p_hi - p.window) return true;
-      if (!p.causal && k1 > p_lo + p.window) return true;
-    }
-    return false;
-  };
+  // Key tiles needing no per-element mask for any row here: [full_lo, full_hi)
+  // (inside the keys, at or before the first row's diagonal, at or after the
+  // last row's window edge, within the first row's window when not causal).
+  int full_lo, full_hi;
+  {
+    auto floor_div = [](long long a, long long b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+    long long fl = -1, fh = Nk / BN;
+    if (p.window > 0) fl = -floor_div(p.window - p_hi, BN);  // ceil((p_hi - W) / BN)
+    if (p.causal) fh = min(fh, floor_div(p_lo + 1, BN));
+    if (p.window > 0 && !p.causal) fh = min(fh, floor_div(p_lo + p.window + 1, BN));
+    full_lo = (int)max(fl, -1LL);
+    full_hi = (int)max(min(fh, (long long)Nk / BN + 1), -1LL);
+  }
+  auto tile_partial = [&](int kt) -> bool { return !(kt >= full_lo && kt < full_hi); };
 
   f32x16 acc[DB];
 #pragma unroll

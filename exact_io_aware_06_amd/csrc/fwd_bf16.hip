@@ -326,17 +326,23 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       dma16(rs, L + slot + (wave * T::KBPW + i) * 1024, dkoff[i]);
   };
 
+  // Key tiles that need no per-element mask for any row here form one range
+  // [full_lo, full_hi): a tile is full iff it lies inside the keys, ends at or
+  // before the first row's diagonal (causal), starts at or after the last
+  // row's window edge, and (non-causal window) ends within the first row's
+  // window. Computed once; clamped to the tile indices a work-group visits.
+  int full_lo, full_hi;
+  {
+    auto floor_div = [](long long a, long long b) { return a >= 0 ? a / b : -((-a + b - 1) / b); };
+    long long fl = -1, fh = Nk / BN;
+    if (p.window > 0) fl = -floor_div(p.window - p_hi, BN);  // ceil((p_hi - W) / BN)
+    if (p.causal) fh = min(fh, floor_div(p_lo + 1, BN));
+    if (p.window > 0 && !p.causal) fh = min(fh, floor_div(p_lo + p.window + 1, BN));
+    full_lo = (int)max(fl, -1LL);
+    full_hi = (int)max(min(fh, (long long)Nk / BN + 1), -1LL);
+  }
   // Does key tile kt need the per-element mask for any valid row here?
-  auto tile_partial = [&](int kt) -> bool {
-    const long long k0 = (long long)kt * BN, k1 = k0 + BN - 1;
-    if (k1 >= Nk) return true;
-    if (p.causal && k1 > p_lo) return true;
-    if (p.window > 0) {
-      if (k0 < p_hi - p.window) return true;
-      if (!p.causal && k1 > p_lo + p.window) return true;
-    }
-    return false;
-  };
+  auto tile_partial = [&](int kt) -> bool { return !(kt >= full_lo && kt < full_hi); };
 
   f32x16 oacc[T::DB];
 #pragma unroll
