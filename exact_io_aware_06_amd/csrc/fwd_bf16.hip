@@ -473,7 +473,11 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       mask_tile(kt + 1, s_nxt);
     }
 
-    // Block B: O^T += V^T P^T.
+    // Block B: O^T += V^T P^T. Two waves of different work-groups share each
+    // SIMD; while this wave issues its matrix-core products it takes issue
+    // priority, so the matrix core is fed while the other wave runs its
+    // vector work (measured 3 % faster than equal priority).
+    __builtin_amdgcn_s_setprio(2);
     const lds_u8* vt_lds = L + VRING + vslot * T::TILE;
     auto vread = [&](int db, int tt) -> bf16x8 {
       const uint2 lo = lds_tr_b64(vt_lds, voff[db][0] + tt * 16 * T::ROWB);
@@ -520,6 +524,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 2, 1);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     wait_vmem();
     __syncthreads();
     if (t + 1 < ntiles) rescale(mx);
