@@ -439,21 +439,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     if (t + 1 < ntiles) issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
     const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
 
+    // P = exp2(S scale_log2 - msub) of the 32-key blocks [kb0, kb1) of tile t,
+    // rounded to bf16, with both row sums.
+    bf16x8 pf[T::PS];
+    auto softmax = [&](int kb0, int kb1) {
+#pragma unroll
+      for (int kb = kb0; kb < kb1; ++kb)
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          f32x8 pv;
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            pv[i] = fast_exp2(__builtin_fmaf(s_cur[kb][hf * 8 + i], p.scale_log2, -msub));
+          l_f += sum_f32x8(pv);
+          pf[kb * 2 + hf] = to_bf16x8(pv);
+          l_b = sum_bf16x8(pf[kb * 2 + hf], l_b);
+        }
+    };
+    // fp8 Q K^T has half the matrix work of bf16: half of the softmax then runs
+    // beside the P V products of block B instead.
+    constexpr bool kSplit = FP8;
+    constexpr int KB_A = kSplit ? T::KB / 2 : T::KB;
+
     // Block A.
     qk(kslot_next, s_nxt);
-    bf16x8 pf[T::PS];
-#pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        f32x8 pv;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          pv[i] = fast_exp2(__builtin_fmaf(s_cur[kb][hf * 8 + i], p.scale_log2, -msub));
-        l_f += sum_f32x8(pv);
-        pf[kb * 2 + hf] = to_bf16x8(pv);
-        l_b = sum_bf16x8(pf[kb * 2 + hf], l_b);
-      }
+    softmax(0, KB_A);
     // d = 64: explicit interleaving of the two blocks, with the boundary mask
     // between them so that each block is one straight-line region (measured
     // ~7 % faster at d = 64; at d = 128 the compiler's own order is faster).
@@ -497,12 +507,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
       for (int db = 0; db < T::DB; ++db) va[0][db] = vread(db, 0);
 #pragma unroll
-      for (int tt = 0; tt < T::PS; ++tt)
+      for (int tt = 0; tt < T::PS; ++tt) {
+        if (kSplit && tt == 2 * KB_A) softmax(KB_A, T::KB);
 #pragma unroll
         for (int db = 0; db < T::DB; ++db) {
           oacc[db] = mfma32x32x16(va[tt & 1][db], pf[tt], oacc[db]);
           if (tt + 1 < T::PS) va[(tt + 1) & 1][db] = vread(db, tt + 1);
         }
+      }
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * T::DB, 2);
 #pragma unroll
       for (int i = 0; i < T::DB * T::PS; ++i) {
