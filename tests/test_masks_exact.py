@@ -31,6 +31,12 @@ SHAPES = [
     (1, 2, 1, 1300, 1000, 64, 1, 0),       # Nq > Nk: empty rows
     (1, 2, 2, 777, 777, 128, 0, 100),      # two-sided window
     (1, 2, 2, 300, 300, 64, 0, 0),
+    (1, 2, 1, 500, 500, 128, 1, 5000),     # window wider than the keys
+    (1, 2, 1, 640, 640, 128, 1, 64),       # window on a key-tile boundary
+    (1, 2, 1, 700, 900, 64, 1, 1),         # window of one key
+    (1, 2, 2, 640, 640, 128, 0, 65),       # two-sided, one past a tile boundary
+    (1, 2, 1, 1, 1000, 128, 1, 0),         # a single query row
+    (1, 2, 1, 200, 4000, 128, 0, 5000),    # two-sided window wider than the keys
 ]
 
 
