@@ -466,7 +466,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     softmax(0, KB_A);
     // d = 64: explicit interleaving of the two blocks, with the boundary mask
     // between them so that each block is one straight-line region (measured
-    // ~7 % faster at d = 64; at d = 128 the compiler's own order is faster).
+    // ~7 % faster at d = 64). At d = 128 the compiler's own order of block A
+    // is faster, and block B is software-pipelined below.
     constexpr bool kInterleave = (D == 64) && !FP8;
     if constexpr (kInterleave) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
