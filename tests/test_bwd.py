@@ -125,6 +125,7 @@ CASES = [
     (1, 4, 4, 129, 129, 128, 0, 40),    # non-causal window
     (2, 8, 2, 256, 256, 128, 1, 0),
     (1, 2, 2, 1, 1, 64, 1, 0),
+    (1, 33, 1, 130, 130, 64, 1, 0),     # a group of 33 query heads (one partial sum of 33)
 ]
 
 

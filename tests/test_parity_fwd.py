@@ -53,6 +53,7 @@ SMALL = [
     (1, 2, 2, 1, 1, 64, 1, 0),
     (1, 2, 1, 5, 700, 128, 0, 0),     # few queries, many keys
     (3, 6, 3, 64, 64, 64, 1, 3),
+    (1, 40, 1, 130, 130, 128, 1, 0),  # 40 query heads on one K/V head
 ]
 
 
