@@ -15,7 +15,11 @@
 // attention kernels).
 //
 // Split kernel: the work-group walks its chunk in tiles of 128 keys staged
-// through LDS (K as rows, V transposed, as in the prefill kernel); wave w
+// through LDS. Every thread loads whole 16-byte pieces of four consecutive K
+// and V rows with non-temporal loads (the cache is streamed once; with
+// row-contiguous accesses this runs ~7 % faster than cached loads), and
+// stores them as rows: K padded, V XOR-swizzled, read back as V^T with
+// transposing LDS reads as in the prefill kernel. Wave w
 // takes keys [32w, 32w + 32) of each tile and treats the G query heads as the
 // 32 columns of a transposed score tile S^T = K Q^T (columns >= G are zero
 // and discarded); a group of more than 32 query heads is split into blocks of
@@ -71,17 +75,34 @@ struct MergeParams {
 template <int D>
 struct DTile {
   static constexpr int KSTR = D + 8;
-  static constexpr int VSTR = kBN + 8;
-  static constexpr int STAGE = kBN * KSTR + D * VSTR;
+  static constexpr int STAGE = kBN * KSTR + kBN * D;  // K rows (padded), V rows (swizzled)
   static constexpr int DB = D / 32;
   static constexpr int KS = D / 16;
   static constexpr int DCH = D / 8;
   static constexpr int KCH = kBN / 4;
   static constexpr int NB = KCH * DCH / kThreads;  // 4x8 blocks per thread per tile
   static_assert(NB * kThreads == KCH * DCH, "tile blocks must split evenly");
+  static constexpr int VROWB = D * 2;  // bytes per V row in LDS
   // The end-of-chunk combine reuses the tile storage.
   static_assert((4 * 32 * D + 3 * 4 * 32) * 4 <= STAGE * 2, "combine scratch fits");
 };
+
+// V tile in LDS: row-major [key][d] with the 16-byte chunks of each row
+// XOR-swizzled (as in the prefill kernel), so that rows are stored with
+// plain 16-byte writes and the transposing V^T operand reads are free of bank
+// conflicts.
+typedef unsigned u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load16_nt(const uint16_t* p, bool ok) {
+  if (!ok) return make_uint4(0u, 0u, 0u, 0u);
+  const u32x4_nt x = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(p));
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  if (D == 128) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
 
 template <int D, bool PAGED>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p) {
@@ -143,22 +164,36 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   };
 
   uint4 kreg[T::NB][4], vreg[T::NB][4];
+  // V^T operand of the products below, by transposing reads: as a source lane
+  // of its 16-lane group this lane names rows 4g + e (+8 for the second read)
+  // of a 16-key step and dims db*32 + 16hh + 4a'; lane 16hh + i then receives
+  // dims 16hh + i of keys 4g..4g+3 and 8+4g..8+4g+3 of the step, the key order
+  // of this lane's P registers.
+  uint32_t voff[T::DB][2];
+  {
+    const int j = lane & 15, a = j & 3, e = j >> 2, hh = (lane >> 4) & 1;
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const int r = 4 * g + e + 8 * qh;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db) {
+        const int c = 4 * db + 2 * hh + (a >> 1);
+        voff[db][qh] = (uint32_t)(r * T::VROWB + ((c ^ vswz<D>(r)) << 4) + (a & 1) * 8);
+      }
+    }
+  }
   auto load_tile = [&](int t0, int slot) {
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) {
       const int bi = tid + nb * kThreads;
-      const int kc_k = bi / T::DCH, dc_k = bi % T::DCH;
-      const int kc_v = bi % T::KCH, dc_v = bi / T::KCH;
+      const int kc = bi / T::DCH, dc = bi % T::DCH;  // rows 4 kc .. + 3, chunk dc
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int rk = t0 + kc_k * 4 + r;
-        bool okk = rk < hi;
-        const size_t ok_off = row_at(okk ? rk : t0, t0, slot, okk);
-        kreg[nb][r] = load16(p.k + ok_off + dc_k * 8, okk);
-        const int rv = t0 + kc_v * 4 + r;
-        bool okv = rv < hi;
-        const size_t ov_off = row_at(okv ? rv : t0, t0, slot, okv);
-        vreg[nb][r] = load16(p.v + ov_off + dc_v * 8, okv);
+        const int rk = t0 + kc * 4 + r;
+        bool ok = rk < hi;
+        const size_t off = row_at(ok ? rk : t0, t0, slot, ok);
+        kreg[nb][r] = load16_nt(p.k + off + dc * 8, ok);
+        vreg[nb][r] = load16_nt(p.v + off + dc * 8, ok);
       }
     }
   };
@@ -168,19 +203,12 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
 #pragma unroll
     for (int nb = 0; nb < T::NB; ++nb) {
       const int bi = tid + nb * kThreads;
-      const int kc_k = bi / T::DCH, dc_k = bi % T::DCH;
-      const int kc_v = bi % T::KCH, dc_v = bi / T::KCH;
-      const int vpos = (kc_v >> 2) * 16 + (((kc_v & 1) << 1) | ((kc_v >> 1) & 1)) * 4;
+      const int kc = bi / T::DCH, dc = bi % T::DCH;
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        *reinterpret_cast<uint4*>(ks + (kc_k * 4 + r) * T::KSTR + dc_k * 8) = kreg[nb][r];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int w = e >> 1, half = e & 1;
-        uint2 col;
-        col.x = interleave16(u4_get(vreg[nb][0], w), u4_get(vreg[nb][1], w), half);
-        col.y = interleave16(u4_get(vreg[nb][2], w), u4_get(vreg[nb][3], w), half);
-        *reinterpret_cast<uint2*>(vs + (dc_v * 8 + e) * T::VSTR + vpos) = col;
+      for (int r = 0; r < 4; ++r) {
+        const int row = kc * 4 + r;
+        *reinterpret_cast<uint4*>(ks + row * T::KSTR + dc * 8) = kreg[nb][r];
+        *reinterpret_cast<uint4*>(vs + row * D + ((dc ^ vswz<D>(row)) * 8)) = vreg[nb][r];
       }
     }
   };
@@ -254,12 +282,16 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
       pf[hf] = to_bf16x8(pv);
       l_b = sum_bf16x8(pf[hf], l_b);
     }
+    const lds_u8* vl = lds_ptr((void*)vs) + wave * 32 * T::VROWB;  // this wave's 32 keys
 #pragma unroll
-    for (int db = 0; db < T::DB; ++db) {
-      const uint16_t* vp = vs + (db * 32 + l32) * T::VSTR + wave * 32 + g * 8;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int t = 0; t < 2; ++t) oacc[db] = mfma32x32x16(lds_read_bf16x8(vp + t * 16), pf[t], oacc[db]);
-    }
+      for (int db = 0; db < T::DB; ++db) {
+        const uint2 lo = lds_tr_b64(vl, voff[db][0] + t * 16 * T::VROWB);
+        const uint2 hi2 = lds_tr_b64(vl, voff[db][1] + t * 16 * T::VROWB);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi2.x, hi2.y));
+        oacc[db] = mfma32x32x16(va, pf[t], oacc[db]);
+      }
     mfma_drain();
   }
 
