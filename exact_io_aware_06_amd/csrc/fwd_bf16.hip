@@ -22,14 +22,18 @@
 //
 // Online softmax (the pages' running max and running denominator, rescaling
 // the partial output when the maximum grows) is done lazily: the reference
-// maximum used for the exponentials is only moved when a row's new maximum
-// exceeds it by more than 2^8 in the exp2 domain, and it is then set 2^24
-// above the new maximum. The final O / l and LSE = m + ln l are identical in
-// exact arithmetic for any reference value, and in floating point P keeps its
-// relative precision at any magnitude (only terms below ~2^-100 of the row
-// maximum underflow). Bounding the growth keeps P <= 256, far from fp32/bf16
-// overflow; the headroom lets a row's maximum grow by 2^32 before the partial
-// output has to be rescaled, which skips most of the rescaling multiplies.
+// maximum used for the exponentials is only moved when P would exceed 2^8,
+// and it is then set 2^24 above the new maximum (exp2 domain). The final
+// O / l and LSE = m + ln l are identical in exact arithmetic for any
+// reference value, and in floating point P keeps its relative precision at
+// any magnitude (only terms below ~2^-100 of the row maximum underflow).
+// Bounding the growth keeps P <= 256, far from fp32/bf16 overflow; the
+// headroom lets a row's maximum grow by 2^32 before the partial output has to
+// be rescaled, which skips most of the rescaling multiplies. At d = 128 (bf16)
+// the test needs no per-tile maximum: each lane's share of a tile's row sum
+// bounds its P values, so a tile is accepted when that share is at most 2^8
+// and otherwise (rarely) redone against a new reference. The d = 64 and fp8
+// kernels take each tile's row maximum and compare it with the reference.
 //
 // Packed documents ("What Lost, and Why", closing section: the mask restarts
 // at every document boundary) reuse the same kernel: the batch index becomes
@@ -48,6 +52,7 @@
 
 #include <cmath>
 #include <cstdio>
+#include <type_traits>
 
 #include "common.hpp"
 #include "launch.hpp"
@@ -169,7 +174,8 @@ __device__ __forceinline__ void decode_workgroup(const FwdParams& p, int id, int
 }
 
 template <int D, bool COUNT, bool FP8 = false>
-__global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 && !FP8 ? 3 : 2)))
+void fwd_bf16_kernel(FwdParams p) {
   using T = Tile<D, FP8>;
   constexpr int BN = T::BN;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[T::LDS];
@@ -401,6 +407,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     return max_halves(mx);
   };
+  // Tile-sum overflow check instead of a per-tile row maximum (bf16, d = 128;
+  // the fp8 kernel computes half of its softmax in block B, and at d = 64 the
+  // redo path costs register spills, so both keep the per-tile maximum). A
+  // lane's share of a tile's row sum bounds each of its P values, so
+  // accepting tiles whose share is at most 2^8 keeps every P at or below 2^8,
+  // the same bound the maximum-based test gives.
+  constexpr bool kSumCheck = !FP8 && D == 128;
+  constexpr float kSumLimit = 256.0f;
   // Move the reference maximum (and rescale O and the sums) if the new
   // tile's maximum exceeds it by more than the threshold.
   auto rescale = [&](float mx) {
@@ -426,22 +440,26 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
   //            tile t (vector ALU);
   //   block B: O += P V of tile t beside mask and row max of tile t+1;
   //   barrier, then the (rare) rescale for tile t+1.
-  // K(t+1) sits in ring slot kslot_next, V(t) in ring slot vslot. The last step
-  // computes a discarded extra score tile, which keeps both blocks free of
-  // branches; MASK_NEXT selects the boundary-tile variant of block B.
-  auto step = [&](int t, int kslot_next, int vslot, f32x16 (&s_cur)[T::KB],
+  // K(t+1) sits in ring slot kslot_next, V(t) in ring slot vslot; MASK_NEXT
+  // selects the boundary-tile variant of block B. The work-group's last step
+  // (LAST, a compile-time tag) has no next tile: its block A is the softmax
+  // alone and block B the P V products alone.
+  auto step = [&](auto last_tag, int t, int kslot_next, int vslot, f32x16 (&s_cur)[T::KB],
                   f32x16 (&s_nxt)[T::KB], bool mask_next) {
+    constexpr bool LAST = decltype(last_tag)::value;
     const int kt = kt_lo + t;
     if (t + 2 < ntiles) {
       issue_k(kt + 2, KRING + (1 - kslot_next) * T::KTILE);
       if (COUNT) ++loaded;
     }
     if (t + 1 < ntiles) issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
-    const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
+    float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
 
     // P = exp2(S scale_log2 - msub) of the 32-key blocks [kb0, kb1) of tile t,
-    // rounded to bf16, with both row sums.
+    // rounded to bf16, with both row sums: added to l_f / l_b directly, or
+    // (kSumCheck) first collected over the tile in tf / tb.
     bf16x8 pf[T::PS];
+    float tf = 0.f, tb = 0.f;
     auto softmax = [&](int kb0, int kb1) {
 #pragma unroll
       for (int kb = kb0; kb < kb1; ++kb)
@@ -451,9 +469,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
 #pragma unroll
           for (int i = 0; i < 8; ++i)
             pv[i] = fast_exp2(__builtin_fmaf(s_cur[kb][hf * 8 + i], p.scale_log2, -msub));
-          l_f += sum_f32x8(pv);
           pf[kb * 2 + hf] = to_bf16x8(pv);
-          l_b = sum_bf16x8(pf[kb * 2 + hf], l_b);
+          if constexpr (kSumCheck) {
+            const bool first = kb == kb0 && hf == 0;
+            tf = first ? sum_f32x8(pv) : tf + sum_f32x8(pv);
+            tb = sum_bf16x8(pf[kb * 2 + hf], first ? 0.f : tb);
+          } else {
+            l_f += sum_f32x8(pv);
+            l_b = sum_bf16x8(pf[kb * 2 + hf], l_b);
+          }
         }
     };
     // fp8 Q K^T has half the matrix work of bf16: half of the softmax then runs
@@ -462,14 +486,14 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     constexpr int KB_A = kSplit ? T::KB / 2 : T::KB;
 
     // Block A.
-    qk(kslot_next, s_nxt);
+    if constexpr (!LAST) qk(kslot_next, s_nxt);
     softmax(0, KB_A);
     // d = 64: explicit interleaving of the two blocks, with the boundary mask
     // between them so that each block is one straight-line region (measured
     // ~7 % faster at d = 64). At d = 128 the compiler's own order of block A
     // is faster, and block B is software-pipelined below.
     constexpr bool kInterleave = (D == 64) && !FP8;
-    if constexpr (kInterleave) {
+    if constexpr (kInterleave && !LAST) {
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #pragma unroll
       for (int i = 0; i < T::KB * T::KS; ++i) {
@@ -478,8 +502,35 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       }
     }
-    mfma_drain();  // s_nxt is read by the vector ALU below
-    if (kInterleave && mask_next) {
+    if constexpr (!LAST) mfma_drain();  // s_nxt is read by the vector ALU below
+    if constexpr (kSumCheck) {
+      // A lane whose share of the tile's row sum exceeds the limit holds a P
+      // above it (or an overflow): move the reference maximum of those rows
+      // above this tile's maximum and redo the tile's softmax (rare).
+      const bool over = !(tf <= kSumLimit);
+      if (wave_any(over)) {
+        // Both halves of a row must move together. The exchange runs in every
+        // lane (under a short-circuit it would run only where `over` is false).
+        const float ov = over ? 1.f : 0.f;
+        const bool row_over = ov + swap_halves(ov) != 0.f;
+        const float mx = row_max(s_cur);
+        mfma_drain();  // O was last written by matrix-core instructions
+        const float m_new = fmaxf(m_ref, mx);
+        const float m_up = m_new + p.head_raw;
+        const float m_set = __builtin_isfinite(m_up) ? m_up : m_new;
+        const float alpha = row_over ? fast_exp2((m_ref - m_set) * p.scale_log2) : 1.f;
+        if (row_over) m_ref = m_set;
+        l_b *= alpha;
+        l_f *= alpha;
+#pragma unroll
+        for (int i = 0; i < T::DB; ++i) oacc[i] *= alpha;
+        msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
+        softmax(0, T::KB);
+      }
+      l_f += tf;
+      l_b += tb;
+    }
+    if (!LAST && kInterleave && mask_next) {
       if (COUNT) ++masked;
       mask_tile(kt + 1, s_nxt);
     }
@@ -523,11 +574,15 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
         if (i < T::DB * (T::PS - 1)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 2);
       }
     }
+    if constexpr (LAST) {
+      __builtin_amdgcn_s_setprio(0);
+      return;
+    }
     if (!kInterleave && mask_next) {
       if (COUNT) ++masked;
       mask_tile(kt + 1, s_nxt);
     }
-    const float mx = row_max(s_nxt);
+    const float mx = kSumCheck ? 0.f : row_max(s_nxt);
     if constexpr (kInterleave) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 1);
 #pragma unroll
@@ -540,7 +595,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     __builtin_amdgcn_s_setprio(0);
     wait_vmem();
     __syncthreads();
-    if (t + 1 < ntiles) rescale(mx);
+    if constexpr (kSumCheck) {
+      // Rows that have seen no key yet take their reference from the next
+      // tile's maximum before its softmax (window and empty-row cases).
+      if (wave_any(m_ref == -kInf)) rescale(row_max(s_nxt));
+    } else {
+      rescale(mx);
+    }
   };
 
   f32x16 sA[T::KB], sB[T::KB];
@@ -563,9 +624,18 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_bf16_kernel(FwdParams p) {
     rescale(row_max(sA));
     __syncthreads();  // K slot 0 is refilled by the first step
   }
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, 1, 0, sA, sB, t + 1 < ntiles && tile_partial(kt_lo + t + 1));
-    if (t + 1 < ntiles) step(t + 1, 0, 1, sB, sA, t + 2 < ntiles && tile_partial(kt_lo + t + 2));
+  using Mid = std::false_type;
+  using Last = std::true_type;
+  int t = 0;
+  for (; t + 2 < ntiles; t += 2) {
+    step(Mid{}, t, 1, 0, sA, sB, tile_partial(kt_lo + t + 1));
+    step(Mid{}, t + 1, 0, 1, sB, sA, tile_partial(kt_lo + t + 2));
+  }
+  if (t + 2 == ntiles) {
+    step(Mid{}, t, 1, 0, sA, sB, tile_partial(kt_lo + t + 1));
+    step(Last{}, t + 1, 0, 1, sB, sA, false);
+  } else if (t + 1 == ntiles) {
+    step(Last{}, t, 1, 0, sA, sB, false);
   }
   mfma_drain();
 

@@ -121,6 +121,28 @@ def test_rising_scores(growth, causal):
     check_lse(to64(lse), lse_ref, label=f"growth={growth} causal={causal}")
 
 
+@pytest.mark.parametrize("jump", [30.0, 100.0, 400.0])
+@pytest.mark.parametrize("causal,window", [(1, 0), (0, 0), (1, 300), (0, 170)])
+def test_score_jump(jump, causal, window):
+    """Scores jump by `jump` at keys 517 and 700 (not on a tile edge), so a
+    tile's exponentials taken against the old reference maximum overflow
+    (to infinity for the larger jumps) and the tile is redone against a new
+    one; with a window, some rows start with no reference at all."""
+    B, H, Hkv, N, d = 1, 2, 1, 900, 128
+    g = torch.Generator().manual_seed(int(jump) + 7 * causal + window)
+    step = (torch.arange(N) >= 517).float() + (torch.arange(N) >= 700).float()
+    q = (1.0 + 0.1 * torch.randn(B, H, N, d, generator=g)).to(torch.bfloat16)
+    k = (step[None, None, :, None] * (jump / d)
+         + 0.3 * torch.randn(B, Hkv, N, d, generator=g) / math.sqrt(d)).to(torch.bfloat16)
+    v = torch.randn(B, Hkv, N, d, generator=g).to(torch.bfloat16)
+    c = cfg(B, H, Hkv, N, N, d, causal, window, scale=1.0)
+    o, lse = run_gpu(c, q, k, v)
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, 1.0, causal, window)
+    label = f"jump={jump} causal={causal} window={window}"
+    check_out(to64(o), o_ref, bf16=True, label=label)
+    check_lse(to64(lse), lse_ref, label=label)
+
+
 # ---------------------------------------------------------------- workloads
 
 
