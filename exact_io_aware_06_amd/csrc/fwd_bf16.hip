@@ -448,11 +448,7 @@ void fwd_bf16_kernel(FwdParams p) {
                   f32x16 (&s_nxt)[T::KB], bool mask_next) {
     constexpr bool LAST = decltype(last_tag)::value;
     const int kt = kt_lo + t;
-    if (t + 2 < ntiles) {
-      issue_k(kt + 2, KRING + (1 - kslot_next) * T::KTILE);
-      if (COUNT) ++loaded;
-    }
-    if (t + 1 < ntiles) issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
+    if (COUNT && t + 2 < ntiles) ++loaded;
     float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
 
     // P = exp2(S scale_log2 - msub) of the 32-key blocks [kb0, kb1) of tile t,
@@ -485,8 +481,15 @@ void fwd_bf16_kernel(FwdParams p) {
     constexpr bool kSplit = FP8;
     constexpr int KB_A = kSplit ? T::KB / 2 : T::KB;
 
-    // Block A.
-    if constexpr (!LAST) qk(kslot_next, s_nxt);
+    // Block A. Its DMA of K(t+2) and V(t+1) has no branch: a step before the
+    // last always has a next tile, and a K tile past the visited range is
+    // issued over an empty range (zeros land in a free ring slot), so the
+    // loads can be scheduled among the matrix-core products.
+    if constexpr (!LAST) {
+      qk(kslot_next, s_nxt);
+      issue_k(t + 2 < ntiles ? kt + 2 : Nk / BN + 1, KRING + (1 - kslot_next) * T::KTILE);
+      issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
+    }
     softmax(0, KB_A);
     // d = 64: explicit interleaving of the two blocks, with the boundary mask
     // between them so that each block is one straight-line region (measured
