@@ -107,18 +107,6 @@ __device__ __forceinline__ uint32_t dma_off(int wave, int lane, int i) {
   return (uint32_t)(r * T::ROWB + (((lane % T::CPR) ^ swz<D>(r)) << 4));
 }
 
-// DMA rows [r0, r0 + ROWS) of a row-major [n, D] bf16 array into an LDS tile;
-// rows at or past n read as zero.
-template <int D, int ROWS>
-__device__ __forceinline__ void dma_rows(const uint16_t* base, long long r0, long long n,
-                                         lds_u8* dst, const uint32_t* doff, int wave) {
-  using T = LTile<D, ROWS>;
-  const uint32_t bytes = r0 < n ? (uint32_t)((n - r0) * T::ROWB) : 0u;
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + r0 * D, bytes);
-#pragma unroll
-  for (int i = 0; i < T::BPW; ++i) dma16(rs, dst + (wave * T::BPW + i) * 1024, doff[i]);
-}
-
 // V^T-style operand: two transposing reads of an LDS tile.
 __device__ __forceinline__ bf16x8 tr_operand(const lds_u8* tile, uint32_t o0, uint32_t o1) {
   const uint2 lo = lds_tr_b64(tile, o0);
@@ -134,6 +122,7 @@ struct BwdParams {
   const uint16_t* dout;
   const float* lse;
   float* delta;  // [B, H, Nq]
+  float* lse2;   // [B, H, Nq]: LSE * log2(e), +inf where LSE = -inf
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
@@ -182,7 +171,9 @@ __device__ __forceinline__ Rows rows_of(const BwdParams& p, int b, int h, int kv
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O), fp32, over the stored (bf16) O.
+// D = rowsum(dO * O), fp32, over the stored (bf16) O; and the LSE in the
+// exp2 domain, with +inf for rows that see no key (so P = 0 on every masked
+// or unmasked score of such a row, with no inf - inf).
 
 template <int D>
 __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p, long long rows) {
@@ -199,7 +190,11 @@ __global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p, long lo
   for (int i = 0; i < 8; ++i) s = __builtin_fmaf((float)x[i], (float)y[i], s);
 #pragma unroll
   for (int w = TPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, 64);
-  if (ok && threadIdx.x % TPR == 0) p.delta[row] = s;
+  if (ok && threadIdx.x % TPR == 0) {
+    p.delta[row] = s;
+    const float l = p.lse[row];
+    p.lse2[row] = l == -kInf ? kInf : l * kLog2e;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -308,21 +303,32 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int i = 0; i < DB; ++i) acc[i] = f32x16{};
 
+  // K and V tile kt into ring slot `slot` (rows at or past Nk read as zero),
+  // issued from inline assembly so that the LDS reads of the current tile do
+  // not wait for it; the barrier at the end of the step is preceded by the
+  // wait.
+  auto issue_tile = [&](long long kt, int slot) {
+    const long long r0 = kt * BN;
+    const uint32_t bytes = r0 < Nk ? (uint32_t)((Nk - r0) * KT::ROWB) : 0u;
+    const long long rr = r0 < Nk ? r0 : 0;
+    const i32x4 rk = rsrc_words(kbase + rr * D, bytes);
+    const i32x4 rv = rsrc_words(vbase + rr * D, bytes);
+#pragma unroll
+    for (int i = 0; i < KT::BPW; ++i) {
+      dma16_async(rk, L + KRING + slot * KT::BYTES + (wave * KT::BPW + i) * 1024, doff[i]);
+      dma16_async(rv, L + VRING + slot * KT::BYTES + (wave * KT::BPW + i) * 1024, doff[i]);
+    }
+  };
   if (ntiles > 0) {
-    dma_rows<D, 64>(kbase, (long long)kt_lo * BN, Nk, L + KRING, doff, wave);
-    dma_rows<D, 64>(vbase, (long long)kt_lo * BN, Nk, L + VRING, doff, wave);
+    issue_tile(kt_lo, 0);
     wait_vmem();
     __syncthreads();
   }
   for (int t = 0; t < ntiles; ++t) {
     const int kt = kt_lo + t;
     const int slot = t & 1;
-    if (t + 1 < ntiles) {
-      dma_rows<D, 64>(kbase, (long long)(kt + 1) * BN, Nk, L + KRING + (1 - slot) * KT::BYTES,
-                      doff, wave);
-      dma_rows<D, 64>(vbase, (long long)(kt + 1) * BN, Nk, L + VRING + (1 - slot) * KT::BYTES,
-                      doff, wave);
-    }
+    // The next tile (an empty range after the last one) into the other slot.
+    issue_tile(t + 1 < ntiles ? kt + 1 : Nk / BN + 1, 1 - slot);
     const lds_u8* kt_lds = L + KRING + slot * KT::BYTES;
     const lds_u8* vt_lds = L + VRING + slot * KT::BYTES;
 
@@ -440,7 +446,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int KS = D / 16, DB = D / 32;
   // LDS: V tile, then the Q ring (2 steps) and the dO ring (2 steps).
   __shared__ __attribute__((aligned(1024))) unsigned char smem[VT::BYTES + 4 * QT::BYTES];
-  __shared__ __attribute__((aligned(16))) float stat[2][2][32];  // [slot][lse2, D][row]
+  // [slot][lse2, D][row]: rows 32..63 of each line take the zeros of the
+  // unused half of a 64-lane copy.
+  __shared__ __attribute__((aligned(256))) float stat[2][2][64];
   lds_u8* const L = lds_ptr(smem);
   constexpr int VOFF = 0, QRING = VT::BYTES, DRING = VT::BYTES + 2 * QT::BYTES;
 
@@ -525,13 +533,28 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   const uint16_t* qbase = p.q + head_q * D;
   const uint16_t* dbase = p.dout + head_q * D;
 
-  // exp2-domain LSE and D of query row r (rows past Nq or seeing no key:
-  // +inf, so every P of the row is 0).
-  auto row_stats = [&](int r, float& l2, float& dl) {
-    const bool ok = r < Nq;
-    const float l = ok ? p.lse[head_q + r] : -kInf;
-    l2 = l == -kInf ? kInf : l * kLog2e;
-    dl = ok ? p.delta[head_q + r] : 0.f;
+  // Copies of step st's rows into ring slot `slot`: Q and dO rows by every
+  // wave, the exp2-domain LSE and D by waves 0 and 1. Rows at or past Nq read
+  // as zero; with their Q and dO rows zero they add nothing to dK or dV. The
+  // copies are issued from inline assembly, so they run on while the LDS
+  // reads of the current step proceed; the caller waits before the barrier
+  // that publishes them.
+  auto issue_step = [&](int st, int slot) {
+    const long long r0 = (long long)st * 32;
+    const uint32_t qbytes = r0 < Nq ? (uint32_t)((Nq - r0) * QT::ROWB) : 0u;
+    const long long rr = r0 < Nq ? r0 : 0;
+    const i32x4 rq = rsrc_words(qbase + rr * D, qbytes);
+    const i32x4 rd = rsrc_words(dbase + rr * D, qbytes);
+#pragma unroll
+    for (int i = 0; i < QT::BPW; ++i) {
+      dma16_async(rq, L + QRING + slot * QT::BYTES + (wave * QT::BPW + i) * 1024, qdoff[i]);
+      dma16_async(rd, L + DRING + slot * QT::BYTES + (wave * QT::BPW + i) * 1024, qdoff[i]);
+    }
+    if (wave < 2) {
+      const uint32_t sbytes = r0 < Nq ? (uint32_t)(min((long long)Nq - r0, 32LL) * 4) : 0u;
+      const float* src = (wave == 0 ? p.lse2 : p.delta) + head_q + rr;
+      dma4_async(rsrc_words(src, sbytes), lds_ptr(&stat[slot][wave][0]), (uint32_t)lane * 4u);
+    }
   };
   // Does step st (rows [32 st, 32 st + 32)) need the per-element mask?
   auto step_partial = [&](int st) -> bool {
@@ -553,24 +576,23 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   }
 
   if (nsteps > 0) {
-    dma_rows<D, 128>(p.v + head_kv * D, k0, Nk, L + VOFF, vdoff, wave);
-    dma_rows<D, 32>(qbase, (long long)st_lo * 32, Nq, L + QRING, qdoff, wave);
-    dma_rows<D, 32>(dbase, (long long)st_lo * 32, Nq, L + DRING, qdoff, wave);
-    if (tid < 32) row_stats(st_lo * 32 + tid, stat[0][0][tid], stat[0][1][tid]);
+    {
+      const uint32_t vbytes = k0 < Nk ? (uint32_t)((Nk - k0) * VT::ROWB) : 0u;
+      const i32x4 rv = rsrc_words(p.v + (head_kv + k0) * D, vbytes);
+#pragma unroll
+      for (int i = 0; i < VT::BPW; ++i)
+        dma16_async(rv, L + VOFF + (wave * VT::BPW + i) * 1024, vdoff[i]);
+    }
+    issue_step(st_lo, 0);
     wait_vmem();
     __syncthreads();
   }
-  float nl2 = 0.f, ndl = 0.f;  // next step's row stats (threads < 32)
   for (int t = 0; t < nsteps; ++t) {
     const int st = st_lo + t;
     const int slot = t & 1;
-    if (t + 1 < nsteps) {
-      dma_rows<D, 32>(qbase, (long long)(st + 1) * 32, Nq, L + QRING + (1 - slot) * QT::BYTES,
-                      qdoff, wave);
-      dma_rows<D, 32>(dbase, (long long)(st + 1) * 32, Nq, L + DRING + (1 - slot) * QT::BYTES,
-                      qdoff, wave);
-      if (tid < 32) row_stats((st + 1) * 32 + tid, nl2, ndl);
-    }
+    // The next step's rows (an empty range after the last step), into the
+    // other slot, whose previous contents the last barrier released.
+    issue_step(t + 1 < nsteps ? st + 1 : (Nq + 31) / 32 + 1, 1 - slot);
     const lds_u8* q_lds = L + QRING + slot * QT::BYTES;
     const lds_u8* d_lds = L + DRING + slot * QT::BYTES;
     const lds_u8* v_lds = L + VOFF;
@@ -631,10 +653,6 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
         dka[db] = mfma32x32x16(tr_operand(q_lds, o0, o1), dsf[tt], dka[db]);
       }
 
-    if (t + 1 < nsteps && tid < 32) {
-      stat[1 - slot][0][tid] = nl2;
-      stat[1 - slot][1][tid] = ndl;
-    }
     wait_vmem();
     __syncthreads();
   }
@@ -751,7 +769,7 @@ hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
 size_t bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d) {
   const size_t delta = ((size_t)B * H * Nq * sizeof(float) + 255) / 256 * 256;
   const size_t part = (H / Hkv > 1) ? (size_t)B * H * Nk * d * sizeof(float) : 0;
-  return delta + 2 * part;
+  return 2 * delta + 2 * part;  // D, exp2-domain LSE, dK and dV partials
 }
 
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
@@ -769,7 +787,8 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   const size_t nb = a.cu_q != nullptr ? 1 : (size_t)a.B;  // packed: one token axis
   const size_t delta = (nb * a.H * a.Nq * sizeof(float) + 255) / 256 * 256;
   p.delta = reinterpret_cast<float*>(ws);
-  p.dk_part = reinterpret_cast<float*>(ws + delta);
+  p.lse2 = reinterpret_cast<float*>(ws + delta);
+  p.dk_part = reinterpret_cast<float*>(ws + 2 * delta);
   p.dv_part = p.dk_part + nb * a.H * a.Nk * a.d;
   p.cu_q = a.cu_q;
   p.cu_k = a.cu_k;

@@ -56,6 +56,45 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rsrc, lds_u8* dst, 
                                            voff, 0, 0, 0);
 }
 
+// The same copy issued from inline assembly, with the buffer descriptor as
+// four SGPRs. The compiler does not see it as a memory operation, so it adds
+// no wait before later LDS reads (it cannot prove that they touch another
+// part of LDS and would otherwise wait for the copy to land). The caller
+// waits itself (wait_vmem) before the data is read, and no compiler-issued
+// LDS copy may be in flight across it (both use M0).
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// M0 is reserved for the compiler's own LDS copies; a kernel that uses these
+// helpers issues all of its copies through them.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+
+__device__ __forceinline__ i32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  return i32x4{(int)__builtin_amdgcn_readfirstlane((uint32_t)a),
+               (int)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu),
+               (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000};
+}
+
+__device__ __forceinline__ void dma16_async(i32x4 rsrc, lds_u8* dst, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "m0");
+}
+
+// 4 bytes per lane: lane L's dword at `voff` lands at dst + 4 L.
+__device__ __forceinline__ void dma4_async(i32x4 rsrc, lds_u8* dst, uint32_t voff) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+               :
+               : "s"(m0v), "v"(voff), "s"(rsrc)
+               : "m0");
+}
+
+#pragma clang diagnostic pop
+
 // s_waitcnt vmcnt(0): every vector-memory load of this wave (DMA included) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 

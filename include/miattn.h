@@ -159,8 +159,9 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  * fp32. Every output element is written by exactly one work-item, so
  * results are deterministic.
  * workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes
- * (else MIATTN_EWORKSPACE): D, plus fp32 dk / dv partials per query head
- * when H > Hkv. Other conventions and errors as for attn_fwd.
+ * (else MIATTN_EWORKSPACE): D and the LSE in the exp2 domain (fp32 per query
+ * row each), plus fp32 dk / dv partials per query head when H > Hkv. Other
+ * conventions and errors as for attn_fwd.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);
 int attn_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,

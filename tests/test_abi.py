@@ -243,8 +243,9 @@ def test_bwd_invalid_arguments(lib):
     assert bwd(lib, B=0, q=NULL, k=NULL, v=NULL, o=NULL, do=NULL, lse=NULL, dq=NULL, dk=NULL,
                dv=NULL, ws=NULL) == OK
     # workspace: D (256-byte aligned), plus fp32 dk/dv partials per query head with GQA
-    assert lib.attn_bwd_workspace_bytes(1, 4, 4, 100, 50, 64) == 1792  # 1600 B rounded to 256
-    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 100, 50, 64) == 1792 + 2 * 4 * 50 * 64 * 4
+    # D and the exp2-domain LSE, 1600 B each rounded to 256, plus (G > 1) fp32 dK / dV partials
+    assert lib.attn_bwd_workspace_bytes(1, 4, 4, 100, 50, 64) == 2 * 1792
+    assert lib.attn_bwd_workspace_bytes(1, 4, 2, 100, 50, 64) == 2 * 1792 + 2 * 4 * 50 * 64 * 4
     assert lib.attn_bwd_workspace_bytes(1, 6, 4, 10, 10, 64) == 0
 
 
