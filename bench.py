@@ -177,7 +177,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
-    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens",
+    ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens", "window",
                                        "paged", "backward", "fp8", "packed_backward"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
@@ -258,6 +258,11 @@ def main():
     q8, k8, v8b, q8_ds, k8_ds = synth.inputs.fp8_prefill_inputs(cp, seed=0, device=dev)
     o8 = torch.empty_like(o)
     lse8 = torch.empty_like(lse)
+    # The causal sliding-window prefill (window 4096 over 32768 tokens).
+    cw = synth.CONFIGS["window4096_gqa_n32768_d128"]
+    qw, kw, vw = synth.prefill_inputs(cw, seed=0, device=dev)
+    ow = torch.empty_like(qw)
+    lsew = torch.empty(cw.B, cw.H, cw.Nq, dtype=torch.float32, device=dev)
     # Backward of the headline prefill: the forward's O and LSE, a seeded dO.
     dout = synth.gen_normal((cp.B, cp.H, cp.Nq, cp.d), 0, 4, 0, "bf16", 1.0, dev)
     dq_b, dk_b, dv_b = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -281,6 +286,8 @@ def main():
             qp, kp, vp, op, lsep, dout_p, cu_dev, cu_dev, max(pk_lens), max(pk_lens),
             scale=cpk.scale, causal=cpk.causal, window=cpk.window, dq=dqp, dk=dkp, dv=dvp,
             workspace=bws_p),
+        "window": lambda: mi.attn_fwd(qw, kw, vw, scale=cw.scale, causal=cw.causal,
+                                      window=cw.window, out=ow, lse=lsew),
         "fp8": lambda: mi.attn_fwd_fp8(q8, k8, v8b, q8_ds, k8_ds, scale=cp.scale,
                                        causal=cp.causal, window=cp.window, out=o8, lse=lse8),
         "backward": lambda: mi.attn_bwd(q, k, v, o, lse, dout, scale=cp.scale,
@@ -292,8 +299,8 @@ def main():
                                               workspace=ws),
     }
     core = ["prefill", "decode", "fp32"]
-    ext = [] if args.no_extensions else ["fp8", "packed", "packed_backward", "kvlens", "paged",
-                                         "backward"]
+    ext = [] if args.no_extensions else ["window", "fp8", "packed", "packed_backward", "kvlens",
+                                         "paged", "backward"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -352,6 +359,7 @@ def main():
     pg_bytes = accounting.decode_paged_bytes(cg.H, cg.Hkv, kv_lens, cg.d, page_size,
                                              window=cg.window)
     bwd_flops = accounting.backward_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
+    win_flops = accounting.prefill_flops(cw.B, cw.H, cw.Nq, cw.Nk, cw.d, cw.causal, cw.window)
     if args.only != "all":
         xs = ms[args.only]
         val, unit = {"prefill": (pre_tflops, "TFLOP/s"), "decode": (dec_gbs, "GB/s"),
@@ -361,6 +369,7 @@ def main():
                      "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s"),
                      "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "fp8": (rate(pre_flops, mean(xs)) / 1e12, "TFLOP/s"),
+                     "window": (rate(win_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "packed_backward": (rate(2.5 * pk_flops, mean(xs)) / 1e12,
                                          "TFLOP/s")}[args.only]
         print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
@@ -408,6 +417,16 @@ def main():
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_for("decode")},
     }
+    if "window" in ms:
+        w_tf = rate(win_flops, mean(ms["window"])) / 1e12
+        out["window_prefill"] = {
+            "workload": f"causal sliding-window GQA prefill B{cw.B} H{cw.H} Hkv{cw.Hkv} "
+                        f"N{cw.Nq} d{cw.d} bf16, window {cw.window}, scale 1/sqrt(d)",
+            "algorithmic_flops": win_flops,
+            "algorithmic_bytes": accounting.prefill_bytes(cw.B, cw.H, cw.Hkv, cw.Nq, cw.Nk, cw.d),
+            "ms": round(mean(ms["window"]), 4), "ms_min": round(min(ms["window"]), 4),
+            "value": round(w_tf, 2), "unit": "TFLOP/s",
+            "frac_peak": round(w_tf / PEAK_BF16_TFLOPS, 4)}
     if "packed" in ms:
         pk_tf = rate(pk_flops, mean(ms["packed"])) / 1e12
         out["packed_prefill"] = {
