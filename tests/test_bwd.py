@@ -122,6 +122,8 @@ CASES = [
     (1, 4, 1, 150, 333, 128, 1, 70),
     (1, 2, 2, 77, 200, 128, 1, 0),      # Nq < Nk: a cached prefix
     (1, 2, 1, 260, 100, 64, 1, 0),      # Nq > Nk: leading rows see nothing
+    (1, 4, 2, 300, 170, 128, 1, 0),     # the same at d = 128 (LSE = -inf rows in every step)
+    (1, 2, 1, 300, 120, 128, 0, 30),    # two-sided window, Nq > Nk: rows 0..149 see nothing
     (1, 4, 4, 129, 129, 128, 0, 40),    # non-causal window
     (2, 8, 2, 256, 256, 128, 1, 0),
     (1, 2, 2, 1, 1, 64, 1, 0),
