@@ -365,7 +365,7 @@ const char* attn_strerror(int status) {
     case MIATTN_EINVAL: return "invalid argument";
     case MIATTN_EUNSUPPORTED: return "unsupported configuration";
     case MIATTN_ELAUNCH: return "kernel launch failed";
-    case MIATTN_EWORKSPACE: return "decode workspace missing or too small";
+    case MIATTN_EWORKSPACE: return "workspace missing or too small";
     case MIATTN_ENODEVICE: return "no HIP device available";
     default: return "unknown status";
   }

@@ -44,8 +44,8 @@
  *   stream    a hipStream_t (NULL = the null stream). Work is enqueued
  *             asynchronously; no entry point synchronises.
  *
- * Ownership: the caller owns every buffer, including the decode workspace,
- * and keeps it alive until the stream work completes. The library allocates
+ * Ownership: the caller owns every buffer, including the decode and backward
+ * workspaces, and keeps it alive until the stream work completes. The library allocates
  * and frees no device memory, keeps no pointer after returning, and holds no
  * per-call state. Calls are thread-safe.
  *
@@ -67,7 +67,7 @@ extern "C" {
 #define MIATTN_EINVAL       -1 /* bad argument: null pointer, negative size, H % Hkv, ... */
 #define MIATTN_EUNSUPPORTED -2 /* valid but not built: d not 64/128, sizes past 32-bit grids */
 #define MIATTN_ELAUNCH      -3 /* the HIP runtime refused a launch */
-#define MIATTN_EWORKSPACE   -4 /* decode workspace NULL or smaller than required */
+#define MIATTN_EWORKSPACE   -4 /* workspace NULL or smaller than required */
 #define MIATTN_ENODEVICE    -5 /* no HIP device is visible to this process */
 
 /*
