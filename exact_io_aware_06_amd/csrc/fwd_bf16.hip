@@ -505,7 +505,9 @@ void fwd_bf16_kernel(FwdParams p) {
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
       }
     }
-    if constexpr (!LAST) mfma_drain();  // s_nxt is read by the vector ALU below
+    // s_nxt is read by the vector ALU below (mask, row max). With the tile-sum
+    // test (d = 128) its first vector read comes after the P V products.
+    if constexpr (!LAST && !kSumCheck) mfma_drain();
     if constexpr (kSumCheck) {
       // A lane whose share of the tile's row sum exceeds the limit holds a P
       // above it (or an overflow): move the reference maximum of those rows
