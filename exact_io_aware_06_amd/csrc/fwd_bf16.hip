@@ -507,7 +507,7 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     // s_nxt is read by the vector ALU below (mask, row max). With the tile-sum
     // test (d = 128) its first vector read comes after the P V products.
-    if constexpr (!LAST && !kSumCheck) mfma_drain();
+    if constexpr (!LAST && (!kSumCheck || kInterleave)) mfma_drain();
     if constexpr (kSumCheck) {
       // A lane whose share of the tile's row sum exceeds the limit holds a P
       // above it (or an overflow): move the reference maximum of those rows
