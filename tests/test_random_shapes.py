@@ -1,0 +1,67 @@
+"""Seeded random-shape parity sweeps of the forward and the backward.
+
+The fixed case lists elsewhere pick shapes by hand; these draw them: query
+and key counts from 1 to 700 (Nq > Nk, Nq < Nk and ragged tails of every
+tile size), d in {64, 128}, group sizes 1 to 8, causal or not, no window or
+a window from 1 to 300 keys, and plain or sharpened logits (which drive the
+online softmax's reference maximum to move often). Every draw is a fixed
+function of its index, so a failure names a reproducible case. Forward
+outputs are held to the forward tolerances of helpers.py; gradients to the
+derived element-wise bound of test_bwd.py.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import check_lse, check_out, to64
+import exact_io_aware_06_amd as mi
+from test_bwd import check as check_bwd
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def draw(i: int):
+    """Shape, flags and inputs of random case i."""
+    r = np.random.default_rng(1000 + i)
+    d = int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4, 8]))
+    Hkv = int(r.integers(1, 3))
+    B = int(r.integers(1, 3))
+    Nq = int(r.integers(1, 701))
+    Nk = int(r.integers(1, 701)) if r.random() < 0.5 else Nq
+    causal = int(r.random() < 0.6)
+    window = 0 if r.random() < 0.5 else int(r.integers(1, 301))
+    sharp = r.random() < 0.3
+    mult = 3.0 * d ** -0.25 if sharp else 1.0
+    scale = 1.0 if sharp else float(np.float32(1 / math.sqrt(d)))
+    g = torch.Generator().manual_seed(7000 + i)
+    H = Hkv * G
+    f = lambda *s: (torch.randn(*s, generator=g) * mult).to(torch.bfloat16)
+    q, k = f(B, H, Nq, d), f(B, Hkv, Nk, d)
+    v = torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16)
+    do = torch.randn(B, H, Nq, d, generator=g).to(torch.bfloat16)
+    label = f"case {i}: B{B} H{H} Hkv{Hkv} Nq{Nq} Nk{Nk} d{d} causal{causal} window{window} sharp{int(sharp)}"
+    return q, k, v, do, scale, causal, window, label
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_forward(i):
+    q, k, v, _, scale, causal, window, label = draw(i)
+    o, lse = mi.attn_fwd(q.to(DEV), k.to(DEV), v.to(DEV), scale=scale, causal=causal,
+                         window=window)
+    torch.cuda.synchronize()
+    o_ref, lse_ref = oracle.attention_ref(q, k, v, scale, causal, window)
+    check_out(to64(o), o_ref, bf16=True, label=label)
+    check_lse(to64(lse), lse_ref, label=label)
+
+
+@pytest.mark.parametrize("i", range(40, 56))
+def test_random_backward(i):
+    q, k, v, do, scale, causal, window, label = draw(i)
+    check_bwd(q, k, v, do, scale, causal, window, label=label)
