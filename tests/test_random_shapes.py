@@ -65,3 +65,70 @@ def test_random_forward(i):
 def test_random_backward(i):
     q, k, v, do, scale, causal, window, label = draw(i)
     check_bwd(q, k, v, do, scale, causal, window, label=label)
+
+
+def draw_decode(i: int):
+    """A decode case: batch, heads, head size, split count and window, with
+    per-sequence cache lengths (0 to 2000, some sequences empty)."""
+    r = np.random.default_rng(2000 + i)
+    d = int(r.choice([64, 128]))
+    G = int(r.choice([1, 2, 4, 8, 16, 40]))
+    Hkv = int(r.integers(1, 3))
+    B = int(r.integers(1, 6))
+    lens = [int(x) if r.random() > 0.1 else 0 for x in r.integers(1, 2001, size=B)]
+    Nk = max(max(lens), 1)
+    splits = min(int(r.choice([0, 1, 2, 3, 16, 64])), Nk)  # at most Nk (else EINVAL)
+    window = 0 if r.random() < 0.6 else int(r.integers(1, 400))
+    ps = int(r.choice([1, 16, 64]))
+    scale = float(np.float32(1 / math.sqrt(d)))
+    label = (f"decode case {i}: B{B} H{Hkv * G} Hkv{Hkv} d{d} lens{lens} splits{splits} "
+             f"window{window} page{ps}")
+    return r, B, Hkv * G, Hkv, d, lens, Nk, splits, window, ps, scale, label
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_decode(i):
+    """Contiguous caches at full length, the same caches with per-sequence
+    lengths, and the same keys in a shuffled page pool, against the oracle."""
+    r, B, H, Hkv, d, lens, Nk, splits, window, ps, scale, label = draw_decode(i)
+    g = torch.Generator().manual_seed(9000 + i)
+    q = torch.randn(B, H, d, generator=g).to(torch.bfloat16)
+    kc = torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16)
+    vc = torch.randn(B, Hkv, Nk, d, generator=g).to(torch.bfloat16)
+    qd, kd, vd = q.to(DEV), kc.to(DEV), vc.to(DEV)
+    o, lse = mi.attn_decode(qd, kd, vd, scale=scale, window=window, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_ref(q, kc, vc, scale, window)
+    check_out(to64(o), o_ref, bf16=True, label=label + " (full length)")
+    check_lse(to64(lse), l_ref, label=label + " (full length)")
+
+    lens_t = torch.as_tensor(lens, dtype=torch.int32)
+    o, lse = mi.attn_decode_varlen(qd, kd, vd, lens_t.to(DEV), scale=scale, window=window,
+                                   num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, scale, window)
+    check_out(to64(o), o_ref, bf16=True, label=label + " (lengths)")
+    check_lse(to64(lse), l_ref, label=label + " (lengths)")
+
+    # the same keys in pages of ps keys, at shuffled physical positions
+    npp = [-(-n // ps) for n in lens]
+    num_pages = max(sum(npp), 1)
+    perm = r.permutation(num_pages)
+    table = np.zeros((B, max(max(npp), 1)), dtype=np.int32)
+    kp = torch.zeros(num_pages, Hkv, ps, d, dtype=torch.bfloat16)
+    vp = torch.zeros(num_pages, Hkv, ps, d, dtype=torch.bfloat16)
+    nxt = 0
+    for b in range(B):
+        for j in range(npp[b]):
+            pg = int(perm[nxt])
+            nxt += 1
+            table[b, j] = pg
+            n = min(ps, lens[b] - j * ps)
+            kp[pg, :, :n] = kc[b, :, j * ps:j * ps + n]
+            vp[pg, :, :n] = vc[b, :, j * ps:j * ps + n]
+    o, lse = mi.attn_decode_paged(qd, kp.to(DEV), vp.to(DEV), torch.from_numpy(table).to(DEV),
+                                  lens_t.to(DEV), scale=scale, window=window, num_splits=splits)
+    torch.cuda.synchronize()
+    o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, lens, ps, scale, window)
+    check_out(to64(o), o_ref, bf16=True, label=label + " (paged)")
+    check_lse(to64(lse), l_ref, label=label + " (paged)")
