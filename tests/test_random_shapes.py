@@ -1,4 +1,4 @@
-"""Seeded random-shape parity sweeps of the forward and the backward.
+"""Seeded random-shape parity sweeps of the forward, the backward and decode.
 
 The fixed case lists elsewhere pick shapes by hand; these draw them: query
 and key counts from 1 to 700 (Nq > Nk, Nq < Nk and ragged tails of every
@@ -7,7 +7,10 @@ a window from 1 to 300 keys, and plain or sharpened logits (which drive the
 online softmax's reference maximum to move often). Every draw is a fixed
 function of its index, so a failure names a reproducible case. Forward
 outputs are held to the forward tolerances of helpers.py; gradients to the
-derived element-wise bound of test_bwd.py.
+derived element-wise bound of test_bwd.py. The decode sweep draws batches of
+per-sequence cache lengths (some empty), group sizes up to 40, split counts
+and page sizes, and runs each case on contiguous caches, with the lengths,
+and from a shuffled page pool.
 """
 
 import math
