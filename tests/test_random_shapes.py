@@ -10,7 +10,9 @@ outputs are held to the forward tolerances of helpers.py; gradients to the
 derived element-wise bound of test_bwd.py. The decode sweep draws batches of
 per-sequence cache lengths (some empty), group sizes up to 40, split counts
 and page sizes, and runs each case on contiguous caches, with the lengths,
-and from a shuffled page pool.
+and from a shuffled page pool. The packed sweep draws document counts and
+lengths (documents without queries or keys included) for the packed forward
+and backward.
 """
 
 import math
@@ -135,3 +137,43 @@ def test_random_decode(i):
     o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, lens, ps, scale, window)
     check_out(to64(o), o_ref, bf16=True, label=label + " (paged)")
     check_lse(to64(lse), l_ref, label=label + " (paged)")
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_packed(i):
+    """Packed documents: random document counts and lengths (documents with
+    no queries or no keys included), forward and backward per document."""
+    from test_bwd_varlen import case, run as run_packed
+    from test_bwd import bounds
+    r = np.random.default_rng(3000 + i)
+    n_docs = int(r.integers(1, 7))
+    lq = [int(x) if r.random() > 0.1 else 0 for x in r.integers(1, 400, size=n_docs)]
+    lk = [x if r.random() < 0.6 else int(r.integers(0, 400)) for x in lq]
+    d = int(r.choice([64, 128]))
+    Hkv = int(r.integers(1, 3))
+    H = Hkv * int(r.choice([1, 2, 4]))
+    causal = int(r.random() < 0.6)
+    window = 0 if r.random() < 0.5 else int(r.integers(1, 200))
+    if sum(lq) == 0 or sum(lk) == 0:
+        lq[0], lk[0] = max(lq[0], 1), max(lk[0], 1)
+    q, k, v, do, cu_q, cu_k = case(lq, lk, H, Hkv, d, seed=4000 + i)
+    scale = float(np.float32(1 / math.sqrt(d)))
+    o, lse, dq, dk, dv = run_packed(q, k, v, do, cu_q, cu_k, scale, causal, window)
+    label = f"packed case {i}: docs {lq}/{lk} H{H} Hkv{Hkv} d{d} causal{causal} window{window}"
+    o_ref, l_ref = oracle.attention_varlen_ref(q, k, v, cu_q, cu_k, scale, causal, window)
+    check_out(to64(o), o_ref, bf16=True, label=label)
+    check_lse(to64(lse), l_ref, label=label)
+    for e in range(n_docs):
+        qs, qe, ks, ke = int(cu_q[e]), int(cu_q[e + 1]), int(cu_k[e]), int(cu_k[e + 1])
+        if qe == qs or ke == ks:
+            continue
+        sl = lambda t, a, b: t[None, :, a:b]
+        refs = oracle.attention_bwd_ref(sl(q, qs, qe), sl(k, ks, ke), sl(v, ks, ke),
+                                        sl(do, qs, qe), scale, causal, window, return_terms=True)
+        tq, tk, tv = bounds(sl(q, qs, qe), sl(k, ks, ke), sl(v, ks, ke), sl(do, qs, qe),
+                            o[None, :, qs:qe].cpu(), scale, refs[3], refs[:3])
+        for name, got, ref, tol in (("dq", dq[None, :, qs:qe], refs[0], tq),
+                                    ("dk", dk[None, :, ks:ke], refs[1], tk),
+                                    ("dv", dv[None, :, ks:ke], refs[2], tv)):
+            ratio = np.abs(to64(got) - ref) / tol
+            assert ratio.max(initial=0.0) <= 1.0, f"{label} doc {e} {name}: err/bound {ratio.max():.3f}"
