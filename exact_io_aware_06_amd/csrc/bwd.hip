@@ -524,6 +524,12 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
 
   LOffsets<D> lo;
   lo.init(lane);
+  // The swizzle permutes 16-byte chunks by XOR, so the offset of k-step ks
+  // is that of k-step 0 with (ks << 5) XORed in, and that of dim block db of
+  // a transposing read is block 0's with (db << 6) XORed in.
+  uint32_t rb = lo.row_off[0];
+  uint32_t vb = lo.row_off[0] + wave * 32 * VT::ROWB;  // this wave's V rows
+  uint32_t tb0 = lo.tr_off[0][0], tb1 = lo.tr_off[0][1];
   uint32_t qdoff[QT::BPW], vdoff[VT::BPW];
 #pragma unroll
   for (int i = 0; i < QT::BPW; ++i) qdoff[i] = dma_off<D, 32>(wave, lane, i);
@@ -599,13 +605,51 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
 
     // S = Q K^T and dP = dO V^T (query rows as rows, this wave's keys as
     // columns): lane (g, l32) holds key l32 for rows 8 c + 4 g + (0..3).
+    // The bases are re-declared opaque each step so the compiler derives
+    // the per-k-step offsets (an XOR each) instead of holding them all.
+    asm volatile("" : "+v"(rb), "+v"(vb), "+v"(tb0), "+v"(tb1));
+    // Operands of k-step ks + 1 are read while the products of ks issue.
     f32x16 s = f32x16{}, dp = f32x16{};
+    bf16x8 qa = lds_b128(q_lds, rb), da = lds_b128(d_lds, rb), va = lds_b128(v_lds, vb);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-      s = mfma32x32x16(lds_b128(q_lds, lo.row_off[ks]), kf[ks], s);
-      // V operand: row (key) wave*32 + l32, dims 16 ks + 8 g .. + 8
-      dp = mfma32x32x16(lds_b128(d_lds, lo.row_off[ks]),
-                        lds_b128(v_lds, lo.row_off[ks] + wave * 32 * VT::ROWB), dp);
+      bf16x8 qn = qa, dn = da, vn = va;
+      if (ks + 1 < KS) {
+        qn = lds_b128(q_lds, rb ^ ((ks + 1) << 5));
+        dn = lds_b128(d_lds, rb ^ ((ks + 1) << 5));
+        vn = lds_b128(v_lds, vb ^ ((ks + 1) << 5));
+      }
+      s = mfma32x32x16(qa, kf[ks], s);
+      dp = mfma32x32x16(da, va, dp);
+      qa = qn;
+      da = dn;
+      va = vn;
+    }
+    // The first transposing operands of the dV / dK products (dim block 0)
+    // are read beside the last products here and land during the softmax.
+    auto tr_ops = [&](int db, bf16x8 (&od)[2], bf16x8 (&oq)[2]) {
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        const uint32_t o0 = (tb0 ^ (db << 6)) + tt * 16 * QT::ROWB;
+        const uint32_t o1 = (tb1 ^ (db << 6)) + tt * 16 * QT::ROWB;
+        od[tt] = tr_operand(d_lds, o0, o1);
+        oq[tt] = tr_operand(q_lds, o0, o1);
+      }
+    };
+    bf16x8 od[2], oq[2];
+    tr_ops(0, od, oq);
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 5);
+#pragma unroll
+    for (int i = 0; i < 2 * KS; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 5);
+      if (i < 2 * (KS - 1)) {
+        if (i & 1)
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 5);
+        else
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 5);
+      } else if (i == 2 * KS - 2) {
+        __builtin_amdgcn_sched_group_barrier(0x100, 8, 5);
+      }
     }
     mfma_drain();
 
@@ -642,16 +686,29 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
       dsf[hf] = to_bf16x8(ds);
     }
 
-    // dV^T += dO^T P and dK^T += Q^T dS (dims as rows, keys as columns).
+    // dV^T += dO^T P and dK^T += Q^T dS (dims as rows, keys as columns);
+    // the operands of dim block db + 1 are read while db's products issue.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db) {
+      bf16x8 odn[2] = {od[0], od[1]}, oqn[2] = {oq[0], oq[1]};
+      if (db + 1 < DB) tr_ops(db + 1, odn, oqn);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
-        const uint32_t o0 = lo.tr_off[db][0] + tt * 16 * QT::ROWB;
-        const uint32_t o1 = lo.tr_off[db][1] + tt * 16 * QT::ROWB;
-        dva[db] = mfma32x32x16(tr_operand(d_lds, o0, o1), pf[tt], dva[db]);
-        dka[db] = mfma32x32x16(tr_operand(q_lds, o0, o1), dsf[tt], dka[db]);
+        dva[db] = mfma32x32x16(od[tt], pf[tt], dva[db]);
+        dka[db] = mfma32x32x16(oq[tt], dsf[tt], dka[db]);
       }
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt) {
+        od[tt] = odn[tt];
+        oq[tt] = oqn[tt];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4 * DB; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 6);
+      if (i < 4 * (DB - 1)) __builtin_amdgcn_sched_group_barrier(0x100, 2, 6);
+    }
 
     wait_vmem();
     __syncthreads();
