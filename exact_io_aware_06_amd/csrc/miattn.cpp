@@ -295,6 +295,9 @@ int attn_bwd(const void* q, const void* k, const void* v, const void* o, const v
   // the dK / dV kernel's 1-D grid: one work-group per (batch, head, 128 keys)
   if ((long long)B * H * ((Nk + 127LL) / 128) > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
   if ((long long)B * Hkv * Nk * d / 8 / 256 > (long long)INT_MAX) return MIATTN_EUNSUPPORTED;
+  // the dK / dV kernel streams the Q and dO rows of a head through 32-bit
+  // buffer offsets
+  if ((long long)Nq * d * 2 > 0xFFFFFFFFLL) return MIATTN_EUNSUPPORTED;
   if (B == 0 || (Nq == 0 && Nk == 0)) return MIATTN_OK;
   const size_t need = miattn::bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d);
   if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
@@ -327,7 +330,7 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
   if ((long long)num_seqs * H * nqt > (long long)INT_MAX ||
       (long long)num_seqs * H * nkt > (long long)INT_MAX)
     return MIATTN_EUNSUPPORTED;
-  if ((long long)total_k * d * 4 > 0xFFFFFFFFLL ||
+  if ((long long)total_k * d * 4 > 0xFFFFFFFFLL || (long long)total_q * d * 2 > 0xFFFFFFFFLL ||
       (long long)Hkv * total_k * d / 8 / 256 > (long long)INT_MAX)
     return MIATTN_EUNSUPPORTED;
   if (num_seqs == 0 || (total_q == 0 && total_k == 0)) return MIATTN_OK;

@@ -160,7 +160,9 @@ int attn_fwd_varlen(const void* q, const void* k, const void* v, void* o, float*
  * results are deterministic.
  * workspace: device memory of at least attn_bwd_workspace_bytes(...) bytes
  * (else MIATTN_EWORKSPACE): D and the LSE in the exp2 domain (fp32 per query
- * row each), plus fp32 dk / dv partials per query head when H > Hkv. Other
+ * row each), plus fp32 dk / dv partials per query head when H > Hkv. One
+ * head's Q (or dO) rows must also stay under 4 GiB (Nq * d * 2 < 2^32; the
+ * packed variant: total_q * d * 2), else MIATTN_EUNSUPPORTED. Other
  * conventions and errors as for attn_fwd.
  */
 size_t attn_bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);

@@ -238,6 +238,9 @@ def test_bwd_invalid_arguments(lib):
     assert bwd(lib, window=-1) == EINVAL
     assert bwd(lib, scale=float("nan")) == EINVAL
     assert bwd(lib, d=96) == EUNSUP
+    # Q / dO rows of one head past 32-bit buffer offsets (2^24 rows of 256 bytes = 2^32)
+    assert bwd(lib, Nq=1 << 24, Nk=16, causal=0) == EUNSUP
+    assert bwd(lib, Nq=(1 << 24) - 1, Nk=16, causal=0, ws=NULL) == EWS
     assert bwd(lib, ws=NULL) == EWS
     assert bwd(lib, ws_bytes=64) == EWS
     assert bwd(lib, B=0, q=NULL, k=NULL, v=NULL, o=NULL, do=NULL, lse=NULL, dq=NULL, dk=NULL,
