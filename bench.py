@@ -11,13 +11,16 @@ the stream the kernels are launched on, around each call inside the timed
 steps.
 
 Beside the step, and timed in a loop of their own over the same number of
-steps, five variants are measured: the prefill with Q and K in fp8, packed-
-document prefill (four 8k contexts filled with documents of log-uniform
-length, the mask restarting at every document), the decode over the same cache
-buffers with a random length per sequence, that decode with its keys in
-16-key pages scattered over one pool, and the backward of the prefill.
+steps, these variants are measured: the causal d = 64 prefill (B4 H16 N2048),
+the causal sliding-window prefill (window 4096 over 32768 tokens), the
+prefill with Q and K in fp8, packed-document prefill (four 8k contexts filled
+with documents of log-uniform length, the mask restarting at every
+document) and its backward, the decode over the same cache buffers with a
+random length per sequence, that decode with its keys in 16-key pages
+scattered over one pool, and the backward of the prefill.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extensions]
+    python bench.py --trace-summary run_kernel_trace.csv --trace-skip W
 """
 
 from __future__ import annotations
@@ -63,6 +66,57 @@ def traffic_for(kind: str):
     return t.get("bytes_per_launch")
 
 
+def trace_summary(path: str, skip: int) -> str:
+    """Markdown table of the library's kernels in a rocprofv3 kernel_trace.csv,
+    over each kernel's launches after its first `skip` (the warm-up calls):
+    launches, mean, median, min and max duration in ns."""
+    import csv
+    import re
+    import statistics
+
+    pat = re.compile(r"miattn::\(anonymous namespace\)::(\w+(<[^()]*>)?)\(")
+    runs = {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            m = pat.search(r["Kernel_Name"])
+            if m is None:
+                continue
+            runs.setdefault(m.group(1), []).append(
+                (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    lines = [f"| kernel | launches (after the first {skip}) | mean ns | median ns | min ns | "
+             f"max ns |", "|---|---|---|---|---|---|"]
+    order = sorted(runs, key=lambda k: -sum(d for _, d in runs[k]))
+    for name in order:
+        ds = [d for _, d in sorted(runs[name])][skip:]
+        if not ds:
+            continue
+        lines.append(f"| `{name}` | {len(ds)} | {statistics.fmean(ds):.0f} | "
+                     f"{statistics.median(ds):.0f} | {min(ds)} | {max(ds)} |")
+    return "\n".join(lines)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def host_cores(threadpool_info):
+    """The host threads the oracle ran on: its BLAS thread pool (the
+    matrix products; NumPy's elementwise work is single-threaded), bounded by
+    the CPUs this process may run on, plus that CPU set and the CPU model."""
+    affinity = len(os.sched_getaffinity(0))
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()
+                if i.get("user_api") == "blas"] or [1])
+    return {"cores": min(blas, affinity), "affinity_cpus": affinity, "blas_threads": blas,
+            "cpu_model": cpu_model()}
+
+
 def cpu_baseline_prefill(cfg, heads: int, q, k, v):
     """The oracle, untuned, on the first `heads` heads of the prefill workload.
 
@@ -79,8 +133,8 @@ def cpu_baseline_prefill(cfg, heads: int, q, k, v):
     oracle.attention_ref(q, k, v, sub.scale, sub.causal, sub.window)
     dt = time.perf_counter() - t0
     flops = accounting.prefill_flops(1, heads, sub.Nq, sub.Nk, sub.d, sub.causal, sub.window)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", **host_cores(threadpool_info),
+            "kind": "oracle",
             "sample": f"{heads} of {cfg.H} heads of the prefill workload (fp64, full score "
                       f"matrix per head), {dt:.2f} s wall",
             "seconds": dt}
@@ -98,8 +152,8 @@ def cpu_baseline_decode(cfg, seqs: int, q, kc, vc):
     oracle.decode_ref(q, kc, vc, sub.scale, sub.window)
     dt = time.perf_counter() - t0
     nbytes = accounting.decode_bytes(seqs, sub.H, sub.Hkv, sub.Nk, sub.d, window=sub.window)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": nbytes / dt / 1e9, "unit": "GB/s", "cores": threads, "kind": "oracle",
+    return {"value": nbytes / dt / 1e9, "unit": "GB/s", **host_cores(threadpool_info),
+            "kind": "oracle",
             "sample": f"{seqs} of {cfg.B} sequences of the decode workload, {dt:.2f} s wall",
             "seconds": dt}
 
@@ -178,7 +232,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=32)
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens", "window",
-                                       "paged", "backward", "fp8", "packed_backward"],
+                                       "paged", "backward", "fp8", "packed_backward",
+                                       "prefill_d64"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
@@ -188,7 +243,17 @@ def main():
                     help="skip the measured matrix-core / read-bandwidth ceilings")
     ap.add_argument("--calib-copy", type=int, default=0, metavar="MIB",
                     help="also run one plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--trace-summary", metavar="CSV",
+                    help="print the steady-state launch durations of this library's kernels "
+                         "from a rocprofv3 kernel_trace.csv (no GPU needed) and exit")
+    ap.add_argument("--trace-skip", type=int, default=None,
+                    help="with --trace-summary: leading launches per kernel to drop "
+                         "(default: --warmup)")
     args = ap.parse_args()
+    if args.trace_summary:
+        skip = args.warmup if args.trace_skip is None else args.trace_skip
+        print(trace_summary(args.trace_summary, skip))
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -218,6 +283,7 @@ def main():
     cp = synth.CONFIGS["causal_gqa_n8192_d128"]
     cd = synth.CONFIGS["decode_b64_nk32768_d128"]
     cf = synth.CONFIGS["f32_n256_d64"]
+    c2 = synth.CONFIGS["causal_b4_h16_n2048_d64"]
     q, k, v = synth.prefill_inputs(cp, seed=0, device=dev)
     qd, kc, vc = synth.decode_inputs(cd, seed=0, device=dev)
     qf, kf, vf = synth.prefill_inputs(cf, seed=0, device=dev)
@@ -258,6 +324,10 @@ def main():
     q8, k8, v8b, q8_ds, k8_ds = synth.inputs.fp8_prefill_inputs(cp, seed=0, device=dev)
     o8 = torch.empty_like(o)
     lse8 = torch.empty_like(lse)
+    # The causal d = 64 prefill (B4 H16 N2048).
+    q2, k2, v2 = synth.prefill_inputs(c2, seed=0, device=dev)
+    o2 = torch.empty_like(q2)
+    lse2 = torch.empty(c2.B, c2.H, c2.Nq, dtype=torch.float32, device=dev)
     # The causal sliding-window prefill (window 4096 over 32768 tokens).
     cw = synth.CONFIGS["window4096_gqa_n32768_d128"]
     qw, kw, vw = synth.prefill_inputs(cw, seed=0, device=dev)
@@ -288,6 +358,8 @@ def main():
             workspace=bws_p),
         "window": lambda: mi.attn_fwd(qw, kw, vw, scale=cw.scale, causal=cw.causal,
                                       window=cw.window, out=ow, lse=lsew),
+        "prefill_d64": lambda: mi.attn_fwd(q2, k2, v2, scale=c2.scale, causal=c2.causal,
+                                           window=c2.window, out=o2, lse=lse2),
         "fp8": lambda: mi.attn_fwd_fp8(q8, k8, v8b, q8_ds, k8_ds, scale=cp.scale,
                                        causal=cp.causal, window=cp.window, out=o8, lse=lse8),
         "backward": lambda: mi.attn_bwd(q, k, v, o, lse, dout, scale=cp.scale,
@@ -299,8 +371,8 @@ def main():
                                               workspace=ws),
     }
     core = ["prefill", "decode", "fp32"]
-    ext = [] if args.no_extensions else ["window", "fp8", "packed", "packed_backward", "kvlens",
-                                         "paged", "backward"]
+    ext = [] if args.no_extensions else ["prefill_d64", "window", "fp8", "packed",
+                                         "packed_backward", "kvlens", "paged", "backward"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -360,6 +432,7 @@ def main():
                                              window=cg.window)
     bwd_flops = accounting.backward_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
     win_flops = accounting.prefill_flops(cw.B, cw.H, cw.Nq, cw.Nk, cw.d, cw.causal, cw.window)
+    d64_flops = accounting.prefill_flops(c2.B, c2.H, c2.Nq, c2.Nk, c2.d, c2.causal, c2.window)
     if args.only != "all":
         xs = ms[args.only]
         val, unit = {"prefill": (pre_tflops, "TFLOP/s"), "decode": (dec_gbs, "GB/s"),
@@ -370,6 +443,7 @@ def main():
                      "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "fp8": (rate(pre_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "window": (rate(win_flops, mean(xs)) / 1e12, "TFLOP/s"),
+                     "prefill_d64": (rate(d64_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "packed_backward": (rate(2.5 * pk_flops, mean(xs)) / 1e12,
                                          "TFLOP/s")}[args.only]
         print(json.dumps({"only": args.only, "ms": round(mean(xs), 4),
@@ -417,6 +491,16 @@ def main():
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                             "traffic": traffic_for("decode")},
     }
+    if "prefill_d64" in ms:
+        d64_tf = rate(d64_flops, mean(ms["prefill_d64"])) / 1e12
+        out["prefill_d64"] = {
+            "workload": f"causal prefill B{c2.B} H{c2.H} Hkv{c2.Hkv} N{c2.Nq} d{c2.d} bf16, "
+                        f"scale 1/sqrt(d)",
+            "algorithmic_flops": d64_flops,
+            "algorithmic_bytes": accounting.prefill_bytes(c2.B, c2.H, c2.Hkv, c2.Nq, c2.Nk, c2.d),
+            "ms": round(mean(ms["prefill_d64"]), 4), "ms_min": round(min(ms["prefill_d64"]), 4),
+            "value": round(d64_tf, 2), "unit": "TFLOP/s",
+            "frac_peak": round(d64_tf / PEAK_BF16_TFLOPS, 4)}
     if "window" in ms:
         w_tf = rate(win_flops, mean(ms["window"])) / 1e12
         out["window_prefill"] = {

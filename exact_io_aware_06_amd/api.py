@@ -109,6 +109,29 @@ def _require(cond, msg):
         raise ValueError(msg)
 
 
+def _check_buffer(t, shape, dtype, device, name):
+    """A caller-provided output buffer must have exactly this shape and dtype,
+    live on `device` and be contiguous (the kernels write it in full)."""
+    _require(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, "
+             f"got {tuple(t.shape)}")
+    _require(t.dtype == dtype, f"{name} must be {dtype}, got {t.dtype}")
+    _require(t.device == device, f"{name} must be on {device}, got {t.device}")
+    _require(t.is_contiguous(), f"{name} must be contiguous")
+
+
+def _workspace(workspace, nbytes, device):
+    """The caller's workspace (checked: on `device`, contiguous, at least
+    `nbytes` bytes) or a new one. Returns (tensor, its size in bytes)."""
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _require(workspace.device == device, f"workspace must be on {device}, got {workspace.device}")
+    _require(workspace.is_contiguous(), "workspace must be contiguous")
+    size = workspace.numel() * workspace.element_size()
+    _require(size >= nbytes, f"workspace holds {size} bytes, {nbytes} needed")
+    return workspace, size
+
+
 def fwd_tile_shape(d: int, is_f32: bool = False):
     lib = load_library()
     bm, bn = ctypes.c_int(), ctypes.c_int()
@@ -143,9 +166,8 @@ def attn_fwd(q, k, v, scale=None, causal=False, window=0, out=None, lse=None):
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
-    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
-    _require(lse.shape == (B, H, Nq) and lse.dtype == torch.float32 and lse.is_contiguous(),
-             "bad lse")
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
+    _check_buffer(lse, (B, H, Nq), torch.float32, q.device, "lse")
     lib = load_library()
     fn = lib.attn_fwd if q.dtype == torch.bfloat16 else lib.attn_fwd_f32
     with torch.cuda.device(q.device):
@@ -176,6 +198,8 @@ def attn_fwd_fp8(q8, k8, v, q_descale, k_descale, scale=None, causal=False, wind
         out = torch.empty(q8.shape, dtype=torch.bfloat16, device=q8.device)
     if lse is None:
         lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q8.device)
+    _check_buffer(out, q8.shape, torch.bfloat16, q8.device, "out")
+    _check_buffer(lse, (B, H, Nq), torch.float32, q8.device, "lse")
     lib = load_library()
     with torch.cuda.device(q8.device):
         _check(lib.attn_fwd_fp8(_ptr(q8), _ptr(k8), _ptr(v), _ptr(out), _ptr(lse), B, H, Hkv,
@@ -242,9 +266,8 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=Non
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device)
-    _require(out.shape == q.shape and out.dtype == q.dtype and out.is_contiguous(), "bad out")
-    _require(lse.shape == (H, total_q) and lse.dtype == torch.float32 and lse.is_contiguous(),
-             "bad lse")
+    _check_buffer(out, q.shape, q.dtype, q.device, "out")
+    _check_buffer(lse, (H, total_q), torch.float32, q.device, "lse")
     lib = load_library()
     with torch.cuda.device(q.device):
         _check(lib.attn_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse),
@@ -303,17 +326,18 @@ def attn_decode(q, k_cache, v_cache, scale=None, window=0, num_splits=0,
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     nbytes = int(lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, int(num_splits)))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_buffer(out, q.shape, torch.bfloat16, q.device, "out")
+    _check_buffer(lse, (B, H), torch.float32, q.device, "lse")
     with torch.cuda.device(q.device):
         _check(lib.attn_decode_splitk(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
                                       _ptr(lse), B, H, Hkv, Nk, d, ctypes.c_float(scale),
                                       int(window), int(num_splits), _ptr(workspace),
-                                      ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+                                      ctypes.c_size_t(ws_bytes), _stream(q.device)))
     return out, lse
 
 
@@ -341,18 +365,19 @@ def attn_decode_varlen(q, k_cache, v_cache, kv_lens, scale=None, window=0, num_s
     scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
     lib = load_library()
     nbytes = int(lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, int(num_splits)))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_buffer(out, q.shape, torch.bfloat16, q.device, "out")
+    _check_buffer(lse, (B, H), torch.float32, q.device, "lse")
     with torch.cuda.device(q.device):
         _check(lib.attn_decode_splitk_varlen(_ptr(q), _ptr(k_cache), _ptr(v_cache),
                                              _ptr(kv_lens), _ptr(out), _ptr(lse), B, H, Hkv, Nk,
                                              d, ctypes.c_float(scale), int(window),
                                              int(num_splits), _ptr(workspace),
-                                             ctypes.c_size_t(workspace.numel()),
+                                             ctypes.c_size_t(ws_bytes),
                                              _stream(q.device)))
     return out, lse
 
@@ -388,18 +413,19 @@ def attn_decode_paged(q, k_pages, v_pages, block_table, kv_lens, scale=None, win
     lib = load_library()
     nbytes = int(lib.attn_decode_workspace_bytes(B, H, Hkv, max_pages * page_size, d,
                                                  int(num_splits)))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((B, H), dtype=torch.float32, device=q.device)
+    _check_buffer(out, q.shape, torch.bfloat16, q.device, "out")
+    _check_buffer(lse, (B, H), torch.float32, q.device, "lse")
     with torch.cuda.device(q.device):
         _check(lib.attn_decode_paged(_ptr(q), _ptr(k_pages), _ptr(v_pages), _ptr(block_table),
                                      _ptr(kv_lens), _ptr(out), _ptr(lse), B, H, Hkv, d,
                                      page_size, num_pages, max_pages, ctypes.c_float(scale),
                                      int(window), int(num_splits), _ptr(workspace),
-                                     ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+                                     ctypes.c_size_t(ws_bytes), _stream(q.device)))
     return out, lse
 
 
@@ -427,16 +453,15 @@ def attn_bwd(q, k, v, o, lse, dout, scale=None, causal=False, window=0, dq=None,
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
-        _require(t.shape == ref.shape and t.dtype == ref.dtype and t.is_contiguous(), f"bad {name}")
+        _check_buffer(t, ref.shape, ref.dtype, q.device, name)
     lib = load_library()
     nbytes = int(lib.attn_bwd_workspace_bytes(B, H, Hkv, Nq, Nk, d))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, q.device)
     with torch.cuda.device(q.device):
         _check(lib.attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq),
                             _ptr(dk), _ptr(dv), B, H, Hkv, Nq, Nk, d, ctypes.c_float(scale),
                             int(bool(causal)), int(window), _ptr(workspace),
-                            ctypes.c_size_t(workspace.numel()), _stream(q.device)))
+                            ctypes.c_size_t(ws_bytes), _stream(q.device)))
     return dq, dk, dv
 
 
@@ -460,18 +485,17 @@ def attn_bwd_varlen(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqle
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
     for t, ref, name in ((dq, q, "dq"), (dk, k, "dk"), (dv, v, "dv")):
-        _require(t.shape == ref.shape and t.dtype == ref.dtype and t.is_contiguous(), f"bad {name}")
+        _check_buffer(t, ref.shape, ref.dtype, q.device, name)
     lib = load_library()
     nbytes = int(lib.attn_bwd_workspace_bytes(1, H, Hkv, total_q, total_k, d))
-    if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=q.device)
+    workspace, ws_bytes = _workspace(workspace, nbytes, q.device)
     with torch.cuda.device(q.device):
         _check(lib.attn_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
                                    _ptr(dq), _ptr(dk), _ptr(dv), _ptr(cu_seqlens_q),
                                    _ptr(cu_seqlens_k), ns, H, Hkv, total_q, total_k,
                                    int(max_seqlen_q), int(max_seqlen_k), d,
                                    ctypes.c_float(scale), int(bool(causal)), int(window),
-                                   _ptr(workspace), ctypes.c_size_t(workspace.numel()),
+                                   _ptr(workspace), ctypes.c_size_t(ws_bytes),
                                    _stream(q.device)))
     return dq, dk, dv
 

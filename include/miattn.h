@@ -84,8 +84,12 @@ int attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
              int B, int H, int Hkv, int Nq, int Nk, int d,
              float scale, int causal, int window, void* stream);
 
-/* Same contract with fp32 q, k, v, o; the whole computation is fp32, with no
- * bf16 rounding anywhere. */
+/* Same contract with fp32 q, k, v, o: softmax(Q K^T / sqrt(d)) V exactly as
+ * defined in "Chapter 3.1 - The Cost of Attention" (section 2), with the
+ * running max / running sum of the online softmax ("Chapter 3.1", section 5;
+ * grasp.study efficient-attention lesson, "Online Softmax"). The whole
+ * computation is fp32 (vector ALU), with no bf16 rounding anywhere: inputs, P
+ * and the output all stay fp32. */
 int attn_fwd_f32(const float* q, const float* k, const float* v, float* o, float* lse,
                  int B, int H, int Hkv, int Nq, int Nk, int d,
                  float scale, int causal, int window, void* stream);
@@ -213,6 +217,15 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
  * the same arguments (else MIATTN_EWORKSPACE). Any group size G = H / Hkv:
  * groups of more than 32 query heads are processed in blocks of 32 (each
  * block reads the group's keys).
+ *
+ * attn_decode_workspace_bytes returns B * H * S * (d + 1) * 4 bytes: the fp32
+ * partial outputs O_s [B, H, S, d] followed by lse_s [B, H, S], where S is
+ * the split count the decode call will use. It takes Hkv and Nk (and not only
+ * B, H, d and num_splits) because num_splits = 0 means "library's choice",
+ * which depends on the number of (sequence, KV head) units B * Hkv and on the
+ * key count Nk (attn_decode_num_splits); with the same arguments as the
+ * decode call it always returns that call's requirement. It returns 0 for
+ * arguments the decode call would reject.
  */
 size_t attn_decode_workspace_bytes(int B, int H, int Hkv, int Nk, int d, int num_splits);
 int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
@@ -308,7 +321,10 @@ int attn_fwd_varlen_tile_counts(const void* q, const void* k, const void* v, voi
 int attn_calib_mfma(int blocks, int iters, float* sink, void* stream);
 int attn_calib_read(const void* buf, size_t bytes, unsigned* sink, int blocks, void* stream);
 
-/* Static string for a status code. */
+/* Static string for a status code (never NULL; "unknown status" for a value
+ * not listed above). The pages define no programming interface, so the status
+ * codes and this call are the library's own error contract: every entry point
+ * reports through its return value and nothing else. */
 const char* attn_strerror(int status);
 
 #ifdef __cplusplus

@@ -4,8 +4,8 @@ Parity on fragmented pools (shuffled physical pages, partial last pages,
 empty and one-key sequences) for several page sizes; bit-identical results
 to the contiguous mixed-length decode on the same keys; shared pages; table
 entries past a sequence's length are never read; an entry outside the pool
-reads as zeros without touching other memory; the paged decode workload at
-full size on sampled sequences.
+reads as zeros without touching other memory. The paged decode workload at
+full size is compared on every output in test_full_size.py.
 """
 
 import math
@@ -134,27 +134,3 @@ def test_paged_entry_outside_pool_reads_zeros():
     o_ref, l_ref = oracle.decode_paged_ref(q, kz, vz, zero_page, lens, ps, 0.088, 0)
     check_out(to64(o), o_ref, label="zero page")
     check_lse(to64(lse), l_ref, label="zero page")
-
-
-def test_paged_workload_full_size_sampled():
-    """B=64, H32 Hkv8 d128, lengths uniform in [1, 32768], 16-key pages scattered."""
-    c = S.PAGED["decode"]
-    ps = S.PAGED["page_size"]
-    lens = S.kv_lengths(0, c.B, c.Nk)
-    table, npg = S.paged_block_table(0, lens, ps)
-    q, kp, vp = S.paged_inputs(c, npg, ps, 0, device=DEV)
-    o, lse = mi.attn_decode_paged(q, kp, vp, torch.from_numpy(table).to(DEV),
-                                  torch.from_numpy(lens).to(DEV), scale=c.scale,
-                                  num_splits=c.splits)
-    torch.cuda.synchronize()
-    og, lg = o.cpu(), lse.cpu()
-    for b in (0, 9, int(np.argmin(lens)), int(np.argmax(lens)), 63):
-        n = int(lens[b])
-        used = table[b:b + 1, :-(-n // ps)]
-        pages = torch.from_numpy(np.unique(used)).to(DEV)
-        remap = np.searchsorted(np.unique(used), used).astype(np.int32)   # local page ids
-        kb, vb = kp[pages].cpu(), vp[pages].cpu()
-        o_ref, l_ref = oracle.decode_paged_ref(q[b:b + 1].cpu(), kb, vb, remap, [n], ps,
-                                               c.scale, c.window)
-        check_out(to64(og[b:b + 1]), o_ref, label=f"g1 b{b}")
-        check_lse(to64(lg[b:b + 1]), l_ref, label=f"g1 b{b}")

@@ -5,13 +5,14 @@ span several tiles with ragged tails, empty documents, documents with more
 or fewer queries than keys, and documents with no keys; exact mask checks
 (q = 0 counts, bit-identical output of the other documents when one is
 changed); per-document tile counts; equal-length documents equal the
-fixed-length kernel bit for bit; the packed workload at full size on
-sampled rows.
+fixed-length kernel bit for bit. (The packed workload at full size is
+compared on every output in test_full_size.py.)
 
 Decode (attn_decode_varlen): parity on mixed lengths including 0 and 1;
 cache rows past a sequence's length never matter; full-length sequences
 equal attn_decode bit for bit; each sequence equals a one-query packed
-prefill over its keys; the mixed-length workload at full size, sampled.
+prefill over its keys. (The mixed-length workload at full size is compared on
+every output in test_full_size.py.)
 """
 
 import math
@@ -191,26 +192,6 @@ def test_varlen_rows_past_max_seqlen_are_not_written():
     assert torch.all(o[:, 128:300] == 3.0) and torch.all(lse[:, 128:300] == 3.0)
 
 
-def test_packed_workload_full_size_sampled():
-    """Four 8k contexts packed with log-uniform documents, H32 Hkv8 d128 causal."""
-    cfg = S.PACKED["packed_24docs_4x8192_d128"]
-    lens = cfg.lengths(0)
-    cu = S.cu_seqlens(lens)
-    total = int(cu[-1])
-    q, k, v = S.packed_inputs(cfg, total, total, seed=0, device="cpu")
-    o, lse = run_varlen(q, k, v, cu, cu, cfg.scale, cfg.causal, cfg.window)
-    rng = np.random.default_rng(0)
-    # first and last rows of every document, plus random rows
-    rows = np.unique(np.concatenate([cu[:-1], cu[1:] - 1, rng.integers(0, total, 64)]))
-    og, lg = o.cpu(), lse.cpu()
-    for h in (0, 5, 17, 31):
-        o_ref, l_ref = oracle.attention_varlen_rows_ref(q, k, v, cu, cu, cfg.scale, cfg.causal,
-                                                        cfg.window, h, rows)
-        check_out(to64(og[h, rows]), o_ref, label=f"p1 h{h}")
-        check_lse(to64(lg[h, rows]), l_ref, label=f"p1 h{h}")
-    assert torch.isfinite(lg).all()  # causal self-attention: every row sees itself
-
-
 # --------------------------------------------------------------------------
 # decode with per-sequence cache lengths
 
@@ -292,27 +273,3 @@ def test_decode_varlen_matches_one_query_packed_prefill():
     check_out(to64(o_pre.transpose(0, 1)), ref_o, label="packed prefill")
     assert float((o_dec.float() - o_pre.transpose(0, 1).float()).abs().max()) <= 2e-2
     check_lse(to64(l_pre.transpose(0, 1)), ref_l, label="packed prefill lse")
-
-
-def test_decode_kvlens_workload_full_size_sampled():
-    """B=64, H32 Hkv8, 32k-key cache slots, lengths uniform in [1, 32768], 16 splits."""
-    c = S.DECODE_KVLENS
-    lens = S.kv_lengths(0, c.B, c.Nk)
-    q, kc, vc = S.decode_inputs(c, 0, device=DEV)
-    o, lse = mi.attn_decode_varlen(q, kc, vc, torch.from_numpy(lens).to(DEV), scale=c.scale,
-                                   num_splits=c.splits)
-    torch.cuda.synchronize()
-    og, lg = o.cpu(), lse.cpu()
-    for b in (0, 7, int(np.argmin(lens)), int(np.argmax(lens)), 63):
-        o_ref, l_ref = _decode_rows(q, kc, vc, lens, c, b)
-        check_out(to64(og[b]), o_ref, label=f"k1 b{b}")
-        check_lse(to64(lg[b]), l_ref, label=f"k1 b{b}")
-    del kc, vc
-
-
-def _decode_rows(q, kc, vc, lens, c, b):
-    """Oracle for sequence b, reading only its first kv_lens[b] cache rows."""
-    n = int(lens[b])
-    qb = q[b:b + 1].cpu()
-    kb, vb = kc[b:b + 1, :, :n].cpu(), vc[b:b + 1, :, :n].cpu()
-    return oracle.decode_kvlens_rows_ref(qb, kb, vb, [n], c.scale, c.window, 0, list(range(c.H)))
