@@ -81,16 +81,18 @@ def trace_summary(path: str, skip: int) -> str:
             m = pat.search(r["Kernel_Name"])
             if m is None:
                 continue
-            runs.setdefault(m.group(1), []).append(
+            # one kernel serves several workloads: the grid tells them apart
+            wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            runs.setdefault((m.group(1), wgs), []).append(
                 (int(r["Start_Timestamp"]), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
-    lines = [f"| kernel | launches (after the first {skip}) | mean ns | median ns | min ns | "
-             f"max ns |", "|---|---|---|---|---|---|"]
+    lines = [f"| kernel | work-groups | launches (after the first {skip}) | mean ns | median ns | "
+             f"min ns | max ns |", "|---|---|---|---|---|---|---|"]
     order = sorted(runs, key=lambda k: -sum(d for _, d in runs[k]))
-    for name in order:
-        ds = [d for _, d in sorted(runs[name])][skip:]
+    for name, wgs in order:
+        ds = [d for _, d in sorted(runs[(name, wgs)])][skip:]
         if not ds:
             continue
-        lines.append(f"| `{name}` | {len(ds)} | {statistics.fmean(ds):.0f} | "
+        lines.append(f"| `{name}` | {wgs} | {len(ds)} | {statistics.fmean(ds):.0f} | "
                      f"{statistics.median(ds):.0f} | {min(ds)} | {max(ds)} |")
     return "\n".join(lines)
 
