@@ -12,6 +12,7 @@ from .api import (  # noqa: F401
     attn_fwd_fp8,
     attn_fwd_varlen,
     attn_decode,
+    attn_decode_splitk_noalloc,
     attn_decode_varlen,
     attn_decode_paged,
     attn_bwd,

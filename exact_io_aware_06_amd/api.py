@@ -79,6 +79,8 @@ def load_library():
         lib.attn_decode_num_splits.restype = I
         lib.attn_decode_splitk.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
         lib.attn_decode_splitk.restype = I
+        lib.attn_decode_splitk_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+        lib.attn_decode_splitk_noalloc.restype = I
         lib.attn_calib_mfma.argtypes = [I, I, P, P]
         lib.attn_calib_mfma.restype = I
         lib.attn_calib_read.argtypes = [P, S, P, I, P]
@@ -338,6 +340,36 @@ def attn_decode(q, k_cache, v_cache, scale=None, window=0, num_splits=0,
                                       _ptr(lse), B, H, Hkv, Nk, d, ctypes.c_float(scale),
                                       int(window), int(num_splits), _ptr(workspace),
                                       ctypes.c_size_t(ws_bytes), _stream(q.device)))
+    return out, lse
+
+
+def attn_decode_splitk_noalloc(q, k_cache, v_cache, out, lse, scale=None, window=0,
+                               num_splits=0):
+    """attn_decode without a workspace: the library's own per-GPU scratch
+    holds the split partials, and nothing is allocated (the caller passes
+    out [B,H,d] bf16 and lse [B,H] fp32). Calls that overlap on one GPU race
+    on that scratch; issue them on one stream. Returns (out, lse)."""
+    import torch
+    _require(q.dim() == 3 and k_cache.dim() == 4 and v_cache.shape == k_cache.shape,
+             "q [B,H,d], caches [B,Hkv,Nk,d]")
+    _require(q.is_cuda and k_cache.device == q.device and v_cache.device == q.device,
+             "tensors must be on the same GPU")
+    _require(q.dtype == torch.bfloat16 and k_cache.dtype == torch.bfloat16
+             and v_cache.dtype == torch.bfloat16, "decode takes bfloat16")
+    _require(q.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous(),
+             "tensors must be contiguous")
+    B, H, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    _require(k_cache.shape[0] == B and k_cache.shape[3] == d, "cache shape mismatch")
+    _check_buffer(out, q.shape, torch.bfloat16, q.device, "out")
+    _check_buffer(lse, (B, H), torch.float32, q.device, "lse")
+    scale = 1.0 / math.sqrt(d) if scale is None else float(scale)
+    lib = load_library()
+    with torch.cuda.device(q.device):
+        _check(lib.attn_decode_splitk_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                              _ptr(lse), B, H, Hkv, Nk, d,
+                                              ctypes.c_float(scale), int(window),
+                                              int(num_splits), _stream(q.device)))
     return out, lse
 
 

@@ -33,11 +33,41 @@
 // lse_s = -inf and weigh nothing.
 
 #include <cstdio>
+#include <mutex>
 
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace miattn {
+
+// Scratch memory of the no-allocation decode entry point: the split partials
+// live here instead of in a caller workspace. Every GPU that runs the library
+// holds its own copy for the life of the process. The host never uses this
+// name as an address (on the host it is only a handle of the symbol); the
+// device address of the current GPU's copy comes from decode_scratch().
+__device__ __attribute__((aligned(256))) unsigned char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch(int device, void** ptr) {
+  *ptr = nullptr;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[device] == nullptr) {
+    // The caller has made `device` current: this resolves that device's copy.
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *ptr = g_scratch_ptr[device];
+  return hipSuccess;
+}
 
 namespace {
 

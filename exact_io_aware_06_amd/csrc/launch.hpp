@@ -80,6 +80,13 @@ hipError_t launch_fwd_f32(const FwdArgs& a, hipStream_t stream);
 size_t decode_workspace_bytes(int B, int H, int d, int splits);
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 
+// Size of the library's own decode scratch (the no-allocation decode entry
+// point); must equal MIATTN_DECODE_SCRATCH_BYTES in miattn.h.
+constexpr size_t kDecodeScratchBytes = (size_t)32 << 20;
+// Device address of `device`'s copy of the decode scratch, resolved once per
+// device; `device` must be the current device on the first call for it.
+hipError_t decode_scratch(int device, void** ptr);
+
 // Backward: workspace = D [B, H, Nq] fp32 (256-byte aligned size), then,
 // when H > Hkv, fp32 dK and dV partials [B, H, Nk, d] each.
 size_t bwd_workspace_bytes(int B, int H, int Hkv, int Nq, int Nk, int d);

@@ -131,11 +131,15 @@ int resolve_splits(int B, int Hkv, int Nk, int num_splits) {
 
 // Paged caches pass block_table != NULL with page_size / max_pages / num_pages
 // and Nk = max_pages * page_size; contiguous caches pass NULL and zeros.
+// The decode workspace: the caller's buffer, or (use_scratch) the library's
+// own scratch of the current device, for callers that cannot allocate.
+enum class Workspace { kCaller, kScratch };
+
 int run_decode(const void* q, const void* k_cache, const void* v_cache, const int* kv_lens,
                void* o, float* lse, int B, int H, int Hkv, int Nk, int d, float scale,
                int window, int num_splits, void* workspace, size_t workspace_bytes,
                const int* block_table, int page_size, int max_pages, int num_pages,
-               void* stream) {
+               void* stream, Workspace ws_kind = Workspace::kCaller) {
   if (B < 0 || H < 1 || Hkv < 1 || Nk < 0) return MIATTN_EINVAL;
   if (H % Hkv != 0) return MIATTN_EINVAL;
   if (window < 0 || !valid_scale(scale)) return MIATTN_EINVAL;
@@ -151,9 +155,33 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache, const in
   if (!paged && Nk > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
   if (paged && num_pages > 0 && (k_cache == nullptr || v_cache == nullptr)) return MIATTN_EINVAL;
   const size_t need = miattn::decode_workspace_bytes(B, H, d, S);
-  if (workspace == nullptr || workspace_bytes < need) return MIATTN_EWORKSPACE;
+  if (ws_kind == Workspace::kScratch) {
+    if (need > miattn::kDecodeScratchBytes) return MIATTN_ESCRATCH;
+  } else if (workspace == nullptr || workspace_bytes < need) {
+    return MIATTN_EWORKSPACE;
+  }
   int st = device_status();
   if (st != MIATTN_OK) return st;
+  if (ws_kind == Workspace::kScratch) {
+    // The scratch copy is the current device's, so the work must run there.
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+      (void)hipGetLastError();
+      return MIATTN_ENODEVICE;
+    }
+    if (stream != nullptr) {
+      hipDevice_t sdev = -1;
+      if (hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev) != hipSuccess) {
+        (void)hipGetLastError();
+        return MIATTN_EINVAL;
+      }
+      if (sdev != dev) return MIATTN_EINVAL;
+    }
+    if (miattn::decode_scratch(dev, &workspace) != hipSuccess) {
+      (void)hipGetLastError();
+      return MIATTN_ELAUNCH;
+    }
+  }
   DecodeArgs a{q,      k_cache, v_cache, o,         lse,     B,          H,
                Hkv,    Nk,      d,       scale,     window,  S,          workspace,
                kv_lens, block_table, page_size, max_pages, num_pages};
@@ -227,6 +255,16 @@ int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache, 
                        int num_splits, void* workspace, size_t workspace_bytes, void* stream) {
   return run_decode(q, k_cache, v_cache, nullptr, o, lse, B, H, Hkv, Nk, d, scale, window,
                     num_splits, workspace, workspace_bytes, nullptr, 0, 0, 0, stream);
+}
+
+static_assert(miattn::kDecodeScratchBytes == MIATTN_DECODE_SCRATCH_BYTES,
+              "the header states the scratch size the library is built with");
+
+int attn_decode_splitk_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               void* o, float* lse, int B, int H, int Hkv, int Nk, int d,
+                               float scale, int window, int num_splits, void* stream) {
+  return run_decode(q, k_cache, v_cache, nullptr, o, lse, B, H, Hkv, Nk, d, scale, window,
+                    num_splits, nullptr, 0, nullptr, 0, 0, 0, stream, Workspace::kScratch);
 }
 
 int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_cache,
@@ -370,6 +408,9 @@ const char* attn_strerror(int status) {
     case MIATTN_ELAUNCH: return "kernel launch failed";
     case MIATTN_EWORKSPACE: return "workspace missing or too small";
     case MIATTN_ENODEVICE: return "no HIP device available";
+    case MIATTN_ESCRATCH:
+      return "the call needs more than the library's decode scratch "
+             "(MIATTN_DECODE_SCRATCH_BYTES); pass a workspace to attn_decode_splitk instead";
     default: return "unknown status";
   }
 }

@@ -69,6 +69,7 @@ extern "C" {
 #define MIATTN_ELAUNCH      -3 /* the HIP runtime refused a launch */
 #define MIATTN_EWORKSPACE   -4 /* workspace NULL or smaller than required */
 #define MIATTN_ENODEVICE    -5 /* no HIP device is visible to this process */
+#define MIATTN_ESCRATCH     -6 /* needs more than the library's own decode scratch */
 
 /*
  * Prefill / training forward, bfloat16 in and out, fp32 LSE.
@@ -233,6 +234,32 @@ int attn_decode_splitk(const void* q, const void* k_cache, const void* v_cache,
                        int B, int H, int Hkv, int Nk, int d, float scale, int window,
                        int num_splits, void* workspace, size_t workspace_bytes,
                        void* stream);
+
+/*
+ * attn_decode_splitk without a workspace argument, for callers that cannot
+ * allocate device memory (code under stream capture into a HIP graph, tight
+ * serving loops, harnesses that forbid allocation). The split partials go to
+ * a scratch array that the library holds in device memory: a fixed
+ * MIATTN_DECODE_SCRATCH_BYTES per GPU, allocated when the library's code is
+ * loaded onto that GPU and kept until the process ends. This call allocates
+ * and frees nothing.
+ *
+ * Arguments, results and errors are those of attn_decode_splitk with no
+ * workspace. A call whose partials (attn_decode_workspace_bytes with the same
+ * arguments) would exceed MIATTN_DECODE_SCRATCH_BYTES returns MIATTN_ESCRATCH
+ * without touching the device. The work runs on the current device: a
+ * non-NULL stream of another device is MIATTN_EINVAL.
+ *
+ * Every call on one GPU shares that GPU's scratch: calls whose work may
+ * overlap on one GPU (other streams, other threads) race and must be ordered
+ * by the caller, e.g. by issuing them on one stream. Each call writes every
+ * partial it reads, so nothing needs clearing between calls.
+ */
+#define MIATTN_DECODE_SCRATCH_BYTES ((size_t)32 << 20)
+int attn_decode_splitk_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                               void* o, float* lse,
+                               int B, int H, int Hkv, int Nk, int d, float scale, int window,
+                               int num_splits, void* stream);
 
 /*
  * Split-K decode over caches whose sequences hold different numbers of keys.

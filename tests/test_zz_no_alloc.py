@@ -1,0 +1,123 @@
+"""The no-allocation decode entry point (attn_decode_splitk_noalloc).
+
+It runs the split-K decode kernels of attn_decode_splitk with the split
+partials in the library's own per-GPU scratch instead of a caller workspace.
+GPU: called through the C ABI, its output must be bit-identical to
+attn_decode_splitk's on the same inputs, on two calls in a row, the second
+smaller (a different head size, split count and batch), and within the
+oracle's tolerances. CPU: requests larger than the scratch are refused before
+any device call.
+"""
+
+import ctypes
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from synth import DecodeConfig
+import exact_io_aware_06_amd as mi
+from exact_io_aware_06_amd import api
+from helpers import check_lse, check_out, to64
+
+MIATTN_EINVAL, MIATTN_ESCRATCH = -1, -6
+SCRATCH_BYTES = 32 << 20
+FAKE = ctypes.c_void_p(0x1000)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    import os
+    if not os.path.exists(api.library_path()):
+        from exact_io_aware_06_amd import build
+        build.build(verbose=False)
+    return api.load_library()
+
+
+def _p(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def noalloc_via_abi(lib, q, kc, vc, scale, window, splits):
+    B, H, d = q.shape
+    Hkv, Nk = kc.shape[1], kc.shape[2]
+    out = torch.full_like(q, 7.0)
+    lse = torch.full((B, H), 7.0, dtype=torch.float32, device=q.device)
+    st = lib.attn_decode_splitk_noalloc(_p(q), _p(kc), _p(vc), _p(out), _p(lse), B, H, Hkv,
+                                        Nk, d, ctypes.c_float(scale), window, splits,
+                                        ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0, lib.attn_strerror(st).decode()
+    return out, lse
+
+
+CASES = [
+    # the larger call first, then a smaller one (other d, splits, batch, group)
+    DecodeConfig("first", 16, 32, 8, 6000, 128, 16, float(np.float32(1 / math.sqrt(128)))),
+    DecodeConfig("second", 3, 8, 2, 700, 64, 5, float(np.float32(1 / 8)), window=90),
+]
+
+
+@pytest.mark.gpu
+def test_noalloc_matches_workspace_decode_two_calls(lib):
+    for i, c in enumerate(CASES):
+        q, kc, vc = synth.decode_inputs(c, seed=30 + i, device="cuda")
+        need = mi.decode_workspace_bytes(c.B, c.H, c.Hkv, c.Nk, c.d, c.splits)
+        assert need <= SCRATCH_BYTES
+        o_na, l_na = noalloc_via_abi(lib, q, kc, vc, c.scale, c.window, c.splits)
+        o_ws, l_ws = mi.attn_decode(q, kc, vc, scale=c.scale, window=c.window,
+                                    num_splits=c.splits)
+        torch.cuda.synchronize()
+        assert torch.equal(o_na, o_ws), f"call {i}: outputs differ"
+        assert torch.equal(l_na, l_ws), f"call {i}: LSE differs"
+        o_ref, l_ref = oracle.decode_ref(q.cpu(), kc.cpu(), vc.cpu(), c.scale, c.window)
+        check_out(to64(o_na), o_ref, bf16=True, label=c.name)
+        check_lse(to64(l_na), l_ref, label=c.name)
+
+
+@pytest.mark.gpu
+def test_noalloc_library_split_choice_and_binding(lib):
+    """num_splits = 0 through the Python binding equals the workspace call."""
+    c = CASES[0].with_(B=5, Nk=3333, splits=0)
+    q, kc, vc = synth.decode_inputs(c, seed=40, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((c.B, c.H), dtype=torch.float32, device="cuda")
+    mi.attn_decode_splitk_noalloc(q, kc, vc, out, lse, scale=c.scale)
+    o_ws, l_ws = mi.attn_decode(q, kc, vc, scale=c.scale)
+    torch.cuda.synchronize()
+    assert torch.equal(out, o_ws) and torch.equal(lse, l_ws)
+
+
+def test_noalloc_refuses_requests_past_the_scratch(lib):
+    # 64 x 32 heads x 64 splits x 129 x 4 B = 67.6 MB of partials > 32 MiB
+    B, H, Hkv, Nk, d, S = 64, 32, 8, 32768, 128, 64
+    assert B * H * S * (d + 1) * 4 > SCRATCH_BYTES
+    st = lib.attn_decode_splitk_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, B, H, Hkv, Nk, d,
+                                        ctypes.c_float(0.088), 0, S, None)
+    assert st == MIATTN_ESCRATCH
+    assert "scratch" in lib.attn_strerror(st).decode()
+    # just under the limit is accepted by validation (it then needs a device)
+    S_ok = SCRATCH_BYTES // (B * H * (d + 1) * 4)
+    assert lib.attn_decode_num_splits(B, Hkv, Nk, S_ok) == S_ok
+
+
+def test_noalloc_argument_errors(lib):
+    args = dict(B=2, H=8, Hkv=2, Nk=100, d=128, scale=0.088, window=0, splits=4)
+
+    def call(**kw):
+        a = dict(args, **kw)
+        return lib.attn_decode_splitk_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, a["B"], a["H"],
+                                              a["Hkv"], a["Nk"], a["d"],
+                                              ctypes.c_float(a["scale"]), a["window"],
+                                              a["splits"], None)
+    assert call(H=7) == MIATTN_EINVAL
+    assert call(window=-1) == MIATTN_EINVAL
+    assert call(scale=0.0) == MIATTN_EINVAL
+    assert call(splits=101) == MIATTN_EINVAL
+    assert call(d=96) == -2
+    null = lib.attn_decode_splitk_noalloc(None, FAKE, FAKE, FAKE, FAKE, 2, 8, 2, 100, 128,
+                                          ctypes.c_float(0.088), 0, 4, None)
+    assert null == MIATTN_EINVAL
+    assert call(B=0) == 0  # nothing to do
