@@ -21,6 +21,8 @@ scattered over one pool, and the backward of the prefill.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extensions]
     python bench.py --trace-summary run_kernel_trace.csv --trace-skip W
+    python bench.py --counter-summary run_counter_collection.csv --trace-skip W
+    python bench.py --write-traffic FETCH.csv WRITE.csv --trace-skip W --calib-copy MIB
 """
 
 from __future__ import annotations
@@ -95,6 +97,88 @@ def trace_summary(path: str, skip: int) -> str:
         lines.append(f"| `{name}` | {wgs} | {len(ds)} | {statistics.fmean(ds):.0f} | "
                      f"{statistics.median(ds):.0f} | {min(ds)} | {max(ds)} |")
     return "\n".join(lines)
+
+
+def _short_kernel(name: str):
+    import re
+    m = re.search(r"miattn::\(anonymous namespace\)::(\w+(<[^()]*>)?)\(", name)
+    return m.group(1) if m else None
+
+
+def counter_table(path: str, skip: int):
+    """{(kernel, work-groups): {counter: [values per dispatch, in order]}} for
+    this library's kernels in a rocprofv3 counter_collection.csv, plus the
+    values of the largest runtime copy kernel (the calibration copy)."""
+    import csv
+    per, copy = {}, {}
+    with open(path, newline="") as f:
+        for r in csv.DictReader(f):
+            name, ctr, val = r["Kernel_Name"], r["Counter_Name"], float(r["Counter_Value"])
+            if "copyBuffer" in name:
+                copy[ctr] = max(copy.get(ctr, 0.0), val)
+                continue
+            k = _short_kernel(name)
+            if k is None:
+                continue
+            wgs = int(r["Grid_Size"]) // max(1, int(r["Workgroup_Size"]))
+            per.setdefault((k, wgs), {}).setdefault(ctr, []).append(
+                (int(r["Dispatch_Id"]), val))
+    out = {key: {c: [v for _, v in sorted(vs)][skip:] for c, vs in d.items()}
+           for key, d in per.items()}
+    return out, copy
+
+
+def counter_summary(path: str, skip: int) -> str:
+    """Markdown: mean value per dispatch of every counter, per kernel and grid."""
+    import statistics
+    tab, copy = counter_table(path, skip)
+    lines = []
+    for (k, wgs), d in sorted(tab.items()):
+        lines.append(f"`{k}`, {wgs} work-groups (launches after the first {skip}):\n")
+        lines.append("| counter | launches | mean per launch |")
+        lines.append("|---|---|---|")
+        for c, vs in sorted(d.items()):
+            if vs:
+                lines.append(f"| `{c}` | {len(vs)} | {statistics.fmean(vs):,.1f} |")
+        lines.append("")
+    if copy:
+        lines.append("Largest runtime copy kernel (the calibration copy): "
+                     + ", ".join(f"`{c}` = {v:,.1f}" for c, v in sorted(copy.items())))
+    return "\n".join(lines)
+
+
+def write_traffic(fetch_csv: str, write_csv: str, skip: int, copy_mib: int) -> dict:
+    """HBM bytes per launch of the headline prefill and decode kernels from a
+    FETCH_SIZE run and a WRITE_SIZE run (KiB per dispatch), each scaled so
+    that the calibration copy of `copy_mib` MiB reads and writes exactly its
+    size; stored in profiles/traffic.json with the digest of the sources."""
+    import statistics
+
+    from exact_io_aware_06_amd import accounting
+    import synth
+    fe, cf = counter_table(fetch_csv, skip)
+    wr, cw = counter_table(write_csv, skip)
+    kib = copy_mib * 1024.0
+    sf, sw = kib / cf["FETCH_SIZE"], kib / cw["WRITE_SIZE"]
+    cp = synth.CONFIGS["causal_gqa_n8192_d128"]
+    cd = synth.CONFIGS["decode_b64_nk32768_d128"]
+    want = {
+        "fwd_bf16": (("fwd_bf16_kernel<128, false, false>", cp.B * cp.H * (cp.Nq // 128)),
+                     accounting.prefill_bytes(cp.B, cp.H, cp.Hkv, cp.Nq, cp.Nk, cp.d)),
+        "decode": (("decode_split_kernel<128, false>", cd.B * cd.Hkv * cd.splits),
+                   accounting.decode_bytes(cd.B, cd.H, cd.Hkv, cd.Nk, cd.d)),
+    }
+    out = {}
+    for kind, (key, alg) in want.items():
+        f = statistics.fmean(fe[key]["FETCH_SIZE"]) * 1024 * sf
+        w = statistics.fmean(wr[key]["WRITE_SIZE"]) * 1024 * sw
+        out[kind] = {"source_digest": source_digest(kind), "bytes_per_launch": int(round(f + w)),
+                     "fetch_bytes": int(round(f)), "write_bytes": int(round(w)),
+                     "algorithmic_bytes": alg, "launches_averaged": len(fe[key]["FETCH_SIZE"]),
+                     "fetch_scale": round(sf, 4), "write_scale": round(sw, 4)}
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+    return out
 
 
 def cpu_model() -> str:
@@ -251,10 +335,24 @@ def main():
     ap.add_argument("--trace-skip", type=int, default=None,
                     help="with --trace-summary: leading launches per kernel to drop "
                          "(default: --warmup)")
+    ap.add_argument("--counter-summary", metavar="CSV",
+                    help="print the mean counter values per launch of this library's kernels "
+                         "from a rocprofv3 counter_collection.csv (no GPU needed) and exit")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="compute the headline kernels' HBM bytes per launch from a FETCH_SIZE "
+                         "and a WRITE_SIZE counter run (with --calib-copy) into "
+                         "profiles/traffic.json and exit")
     args = ap.parse_args()
+    skip = args.warmup if args.trace_skip is None else args.trace_skip
     if args.trace_summary:
-        skip = args.warmup if args.trace_skip is None else args.trace_skip
         print(trace_summary(args.trace_summary, skip))
+        return
+    if args.counter_summary:
+        print(counter_summary(args.counter_summary, skip))
+        return
+    if args.write_traffic:
+        print(json.dumps(write_traffic(*args.write_traffic, skip, args.calib_copy or 1024),
+                         indent=1))
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

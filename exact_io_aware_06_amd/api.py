@@ -37,58 +37,72 @@ def load_library():
     with _lock:
         if _lib is not None:
             return _lib
-        path = library_path()
-        if not os.path.exists(path):
-            raise RuntimeError(
-                f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
-                "from the repository root")
-        lib = ctypes.CDLL(path)
-        P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
-        fwd_args = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
-        lib.attn_fwd.argtypes = fwd_args
-        lib.attn_fwd.restype = I
-        lib.attn_fwd_f32.argtypes = fwd_args
-        lib.attn_fwd_f32.restype = I
-        lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, F, I, I, P]
-        lib.attn_fwd_fp8.restype = I
-        lib.attn_fwd_tile_counts.argtypes = fwd_args[:-1] + [P, P]
-        lib.attn_fwd_tile_counts.restype = I
-        varlen_args = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I]
-        lib.attn_fwd_varlen.argtypes = varlen_args + [P]
-        lib.attn_fwd_varlen.restype = I
-        lib.attn_fwd_varlen_tile_counts.argtypes = varlen_args + [P, P]
-        lib.attn_fwd_varlen_tile_counts.restype = I
-        lib.attn_decode_splitk_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P,
-                                                  S, P]
-        lib.attn_decode_splitk_varlen.restype = I
-        lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P,
-                                          S, P]
-        lib.attn_decode_paged.restype = I
-        lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
-        lib.attn_bwd_workspace_bytes.restype = S
-        lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, S, P]
-        lib.attn_bwd.restype = I
-        lib.attn_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
-                                        F, I, I, P, S, P]
-        lib.attn_bwd_varlen.restype = I
-        lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
-        lib.attn_fwd_tile_shape.restype = I
-        lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
-        lib.attn_decode_workspace_bytes.restype = S
-        lib.attn_decode_num_splits.argtypes = [I, I, I, I]
-        lib.attn_decode_num_splits.restype = I
-        lib.attn_decode_splitk.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
-        lib.attn_decode_splitk.restype = I
-        lib.attn_decode_splitk_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
-        lib.attn_decode_splitk_noalloc.restype = I
-        lib.attn_calib_mfma.argtypes = [I, I, P, P]
-        lib.attn_calib_mfma.restype = I
-        lib.attn_calib_read.argtypes = [P, S, P, I, P]
-        lib.attn_calib_read.restype = I
-        lib.attn_strerror.argtypes = [I]
-        lib.attn_strerror.restype = ctypes.c_char_p
-        _lib = lib
-        return lib
+        _lib = _open(library_path())
+        return _lib
+
+
+def load_variant(path: str):
+    """Load another build of the library (such as the fully fenced race-check
+    build libmiattn_serial.so) with the same C signatures declared."""
+    with _lock:
+        return _open(path)
+
+
+def _open(path: str):
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is not built: run `python -c 'import __graft_entry__ as g; g.build()'` "
+            "from the repository root")
+    lib = ctypes.CDLL(path)
+    _declare(lib)
+    return lib
+
+
+def _declare(lib):
+    P, I, F, S = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    fwd_args = [P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
+    lib.attn_fwd.argtypes = fwd_args
+    lib.attn_fwd.restype = I
+    lib.attn_fwd_f32.argtypes = fwd_args
+    lib.attn_fwd_f32.restype = I
+    lib.attn_fwd_fp8.argtypes = [P, P, P, P, P, I, I, I, I, I, I, F, F, F, I, I, P]
+    lib.attn_fwd_fp8.restype = I
+    lib.attn_fwd_tile_counts.argtypes = fwd_args[:-1] + [P, P]
+    lib.attn_fwd_tile_counts.restype = I
+    varlen_args = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I]
+    lib.attn_fwd_varlen.argtypes = varlen_args + [P]
+    lib.attn_fwd_varlen.restype = I
+    lib.attn_fwd_varlen_tile_counts.argtypes = varlen_args + [P, P]
+    lib.attn_fwd_varlen_tile_counts.restype = I
+    lib.attn_decode_splitk_varlen.argtypes = [P, P, P, P, P, P, I, I, I, I, I, F, I, I, P,
+                                              S, P]
+    lib.attn_decode_splitk_varlen.restype = I
+    lib.attn_decode_paged.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, F, I, I, P,
+                                      S, P]
+    lib.attn_decode_paged.restype = I
+    lib.attn_bwd_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_bwd_workspace_bytes.restype = S
+    lib.attn_bwd.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P, S, P]
+    lib.attn_bwd.restype = I
+    lib.attn_bwd_varlen.argtypes = [P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, I, I,
+                                    F, I, I, P, S, P]
+    lib.attn_bwd_varlen.restype = I
+    lib.attn_fwd_tile_shape.argtypes = [I, I, ctypes.POINTER(I), ctypes.POINTER(I)]
+    lib.attn_fwd_tile_shape.restype = I
+    lib.attn_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.attn_decode_workspace_bytes.restype = S
+    lib.attn_decode_num_splits.argtypes = [I, I, I, I]
+    lib.attn_decode_num_splits.restype = I
+    lib.attn_decode_splitk.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P, S, P]
+    lib.attn_decode_splitk.restype = I
+    lib.attn_decode_splitk_noalloc.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, I, P]
+    lib.attn_decode_splitk_noalloc.restype = I
+    lib.attn_calib_mfma.argtypes = [I, I, P, P]
+    lib.attn_calib_mfma.restype = I
+    lib.attn_calib_read.argtypes = [P, S, P, I, P]
+    lib.attn_calib_read.restype = I
+    lib.attn_strerror.argtypes = [I]
+    lib.attn_strerror.restype = ctypes.c_char_p
 
 
 def _check(status: int):

@@ -328,7 +328,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
     const int kt = kt_lo + t;
     const int slot = t & 1;
     // The next tile (an empty range after the last one) into the other slot.
+    ring_fence_before_copy();
     issue_tile(t + 1 < ntiles ? kt + 1 : Nk / BN + 1, 1 - slot);
+    ring_fence_after_copy();
     const lds_u8* kt_lds = L + KRING + slot * KT::BYTES;
     const lds_u8* vt_lds = L + VRING + slot * KT::BYTES;
 
@@ -598,7 +600,9 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
     const int slot = t & 1;
     // The next step's rows (an empty range after the last step), into the
     // other slot, whose previous contents the last barrier released.
+    ring_fence_before_copy();
     issue_step(t + 1 < nsteps ? st + 1 : (Nq + 31) / 32 + 1, 1 - slot);
+    ring_fence_after_copy();
     const lds_u8* q_lds = L + QRING + slot * QT::BYTES;
     const lds_u8* d_lds = L + DRING + slot * QT::BYTES;
     const lds_u8* v_lds = L + VOFF;

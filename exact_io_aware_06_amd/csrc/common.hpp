@@ -98,6 +98,29 @@ __device__ __forceinline__ void dma4_async(i32x4 rsrc, lds_u8* dst, uint32_t vof
 // s_waitcnt vmcnt(0): every vector-memory load of this wave (DMA included) done.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Race-detector build. With MIATTN_SERIAL_RINGS=1 every copy into an LDS ring
+// slot is fenced on both sides: a barrier before it (every wave has finished
+// reading what the slot held) and, after it, a wait for this wave's copies
+// and a barrier (every wave's copies have landed before anyone reads them).
+// Each kernel also pads every matrix-core block whose results the vector ALU
+// reads. The arithmetic and its order are unchanged, so this build must give
+// bit-identical results to the pipelined one; a difference exposes a missing
+// wait or barrier, or a too-short wait-state pad, in the pipelined kernels.
+#ifndef MIATTN_SERIAL_RINGS
+#define MIATTN_SERIAL_RINGS 0
+#endif
+constexpr bool kSerialRings = MIATTN_SERIAL_RINGS != 0;
+
+__device__ __forceinline__ void ring_fence_before_copy() {
+  if constexpr (kSerialRings) __syncthreads();
+}
+__device__ __forceinline__ void ring_fence_after_copy() {
+  if constexpr (kSerialRings) {
+    wait_vmem();
+    __syncthreads();
+  }
+}
+
 // 16-byte global load that yields zeros when `ok` is false.
 __device__ __forceinline__ uint4 load16(const uint16_t* p, bool ok) {
   uint4 r = make_uint4(0u, 0u, 0u, 0u);

@@ -487,8 +487,10 @@ void fwd_bf16_kernel(FwdParams p) {
     // loads can be scheduled among the matrix-core products.
     if constexpr (!LAST) {
       qk(kslot_next, s_nxt);
+      ring_fence_before_copy();
       issue_k(t + 2 < ntiles ? kt + 2 : Nk / BN + 1, KRING + (1 - kslot_next) * T::KTILE);
       issue(vbase, kt + 1, VRING + (1 - vslot) * T::TILE);
+      ring_fence_after_copy();
     }
     softmax(0, KB_A);
     // d = 64: explicit interleaving of the two blocks, with the boundary mask
@@ -507,7 +509,7 @@ void fwd_bf16_kernel(FwdParams p) {
     }
     // s_nxt is read by the vector ALU below (mask, row max). With the tile-sum
     // test (d = 128) its first vector read comes after the P V products.
-    if constexpr (!LAST && (!kSumCheck || kInterleave)) mfma_drain();
+    if constexpr (!LAST && (!kSumCheck || kInterleave || kSerialRings)) mfma_drain();
     if constexpr (kSumCheck) {
       // A lane whose share of the tile's row sum exceeds the limit holds a P
       // above it (or an overflow): move the reference maximum of those rows
