@@ -145,8 +145,13 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  const int s = blockIdx.x % p.S;
-  const int bhb = blockIdx.x / p.S;
+  // Grid order: split slowest. Consecutive work-groups are different
+  // (sequence, KV head, head block) units of the same split, so the XCDs,
+  // which receive work-groups round-robin, each get the same mix of chunk
+  // sizes (with per-sequence lengths, split s of every sequence in turn).
+  const int nbhb = p.B * p.Hkv * p.HB;
+  const int s = blockIdx.x / nbhb;
+  const int bhb = blockIdx.x - s * nbhb;
   const int hb = bhb % p.HB;
   const int bk = bhb / p.HB;
   const int g0 = hb * 32;               // first query head of this block in the group
