@@ -3,7 +3,8 @@
 Every entry point only enqueues kernels on the caller's stream, allocates
 nothing and never synchronises, so a sequence of calls can be captured once
 and replayed. The graph here holds a causal GQA prefill, its backward, a
-packed-document prefill, a split-K decode and a paged decode. It is replayed
+packed-document prefill, a split-K decode, a paged decode and the
+no-allocation split-K decode. It is replayed
 three times with eager work and synchronisations in between (the outputs are
 overwritten with NaN before each replay), and every replay must reproduce
 the eager results bit for bit: the kernels are deterministic and none reads
@@ -63,8 +64,12 @@ def run_all(x):
     od, ld = mi.attn_decode(x["qd"], x["kc"], x["vc"], scale=s, num_splits=7)
     og, lg = mi.attn_decode_paged(x["qd"], x["kpg"], x["vpg"], x["table"], x["lens"], scale=s,
                                   num_splits=5)
+    # the no-allocation decode (its partials in the library's own scratch)
+    on = torch.empty_like(x["qd"])
+    ln = torch.empty(x["qd"].shape[:2], dtype=torch.float32, device=DEV)
+    mi.attn_decode_splitk_noalloc(x["qd"], x["kc"], x["vc"], on, ln, scale=s, num_splits=7)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "op": op, "lp": lp, "od": od,
-            "ld": ld, "og": og, "lg": lg}
+            "ld": ld, "og": og, "lg": lg, "on": on, "ln": ln}
 
 
 def test_graph_replays_match_eager():
@@ -88,10 +93,17 @@ def test_graph_replays_match_eager():
     for rep in range(3):
         for t in outs.values():
             t.fill_(float("nan"))
-        # eager library work between replays, on the current stream
+        # eager library work between replays, on the current stream; the
+        # no-allocation decode overwrites the scratch with another shape
         mi.attn_fwd(x["q"], x["k"], x["v"], scale=0.05, causal=0)
+        qx, kx = x["qd"][:2].contiguous(), x["kc"][:2, :, :600].contiguous()
+        mi.attn_decode_splitk_noalloc(qx, kx, kx, torch.empty_like(qx),
+                                      torch.empty(qx.shape[:2], device=DEV), scale=0.1,
+                                      num_splits=3 + rep)
         torch.cuda.synchronize()
         graph.replay()
         torch.cuda.synchronize()
         for name, ref in eager.items():
             assert torch.equal(outs[name], ref), f"replay {rep}: {name} differs from the eager call"
+    # the no-allocation decode equals the decode with a workspace
+    assert torch.equal(eager["on"], eager["od"]) and torch.equal(eager["ln"], eager["ld"])
