@@ -20,6 +20,13 @@ on dense row blocks of every head: the first and last two query tiles, the
 rows around the window's edge (4095-4225), every 512th row and a seeded 2 %
 of all rows.
 
+The causal context sweep (B1 H32 Hkv8 d128, N(0,1) inputs, scale 1/sqrt(d),
+N = 1k ... 128k) is compared on every output up to 8k tokens, and from 16k
+on, where the oracle's full score matrix grows to 34-550 GB per run, on dense
+row blocks of all 32 heads: the first and last query tiles, four seeded
+blocks of 128 consecutive rows and every (N/64)-th row, each row against all
+N keys.
+
 The kernels run exactly as in the benchmark (same entry points, same split
 count and tile configuration).
 """
@@ -194,4 +201,45 @@ def test_decode_paged_every_output(seed):
 
     decode_all_sequences(o, lse, ref, c.B, f"{c.name} seed {seed}")
     del kp, vp
+    torch.cuda.empty_cache()
+
+
+SWEEP = [1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072]
+
+
+def sweep_rows(N, seed):
+    rng = np.random.default_rng(2000 + N + seed)
+    rows = set(range(0, 128)) | set(range(N - 128, N)) | set(range(0, N, N // 64))
+    for start in rng.choice(N // 128, size=4, replace=False):
+        rows |= set(range(int(start) * 128, int(start) * 128 + 128))
+    return np.array(sorted(rows), dtype=np.int64)
+
+
+@pytest.mark.parametrize("N", SWEEP)
+def test_causal_context_sweep(N):
+    c = synth.CONFIGS["window4096_gqa_n32768_d128"].with_(name=f"causal{N}", Nq=N, Nk=N,
+                                                          window=0)
+    note(f"{c.name}: GPU")
+    q, k, v = synth.prefill_inputs(c, 0, device=DEV)
+    o, lse = mi.attn_fwd(q, k, v, scale=c.scale, causal=c.causal, window=c.window)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if N <= 8192:
+        qh, kh, vh = q.cpu(), k.cpu(), v.cpu()
+        o_ref, l_ref = oracle.attention_ref(qh, kh, vh, c.scale, c.causal, c.window)
+        og, lg = to64(o), to64(lse)
+        what = "every output"
+    else:
+        rows = sweep_rows(N, 0)
+        o_ref = np.empty((c.H, rows.size, c.d))
+        l_ref = np.empty((c.H, rows.size))
+        kh, vh = k.cpu(), v.cpu()
+        for h in range(c.H):
+            o_ref[h], l_ref[h] = oracle.attention_rows_ref(q, kh, vh, c.scale, c.causal,
+                                                           c.window, 0, h, rows)
+        og, lg = to64(o[0][:, rows]), to64(lse[0][:, rows])
+        what = f"{rows.size} rows x {c.H} heads"
+    note(f"{c.name}: oracle on {what} {time.perf_counter() - t0:.1f} s")
+    compare(og, o_ref, lg, l_ref, f"{c.name} ({what})")
+    del q, k, v, o, lse
     torch.cuda.empty_cache()
