@@ -8,11 +8,11 @@
 //
 // Each query row is owned by D / 32 consecutive lanes, each holding 32 of its
 // dimensions of q and of the output accumulator; a dot product is a 32-term
-// in-lane sum plus a butterfly over those lanes. The four waves of a
+// in-lane sum plus a butterfly over those lanes. The eight waves of a
 // work-group hold the same query rows and split the key tiles between them
-// (wave w takes tiles w, w + 4, ...), each staging its tiles in its own LDS
-// region; their (max, sum, output) partials are merged once at the end, as
-// the online softmax merges any two partial results.
+// (wave w takes tiles w, w + 8, ...), each staging its tiles in its own LDS
+// region with 16-byte loads; their (max, sum, output) partials are merged
+// once at the end, as the online softmax merges any two partial results.
 
 #include <cstdio>
 
@@ -23,7 +23,7 @@ namespace miattn {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
 
 struct F32Params {
@@ -91,11 +91,16 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Params p) {
       const int k0 = kt * BN;
       // this wave's lanes finished reading the previous tile (in-order LDS)
       __builtin_amdgcn_wave_barrier();
-      for (int e = lane; e < BN * D; e += 64) {
-        const int r = e / D, c = e - r * D;
-        const bool ok = k0 + r < p.Nk;
-        ks[e] = ok ? p.k[(head_kv + k0 + r) * D + c] : 0.f;
-        vs[e] = ok ? p.v[(head_kv + k0 + r) * D + c] : 0.f;
+      // the tile's rows are contiguous in memory: 16-byte pieces, rows past
+      // the keys read as zero
+      const float4* kg = reinterpret_cast<const float4*>(p.k + (head_kv + k0) * D);
+      const float4* vg = reinterpret_cast<const float4*>(p.v + (head_kv + k0) * D);
+#pragma unroll
+      for (int e4 = lane; e4 < BN * D / 4; e4 += 64) {
+        const bool ok = k0 + (e4 * 4) / D < p.Nk;
+        const float4 z = make_float4(0.f, 0.f, 0.f, 0.f);
+        reinterpret_cast<float4*>(ks)[e4] = ok ? kg[e4] : z;
+        reinterpret_cast<float4*>(vs)[e4] = ok ? vg[e4] : z;
       }
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
