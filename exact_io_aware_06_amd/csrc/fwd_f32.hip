@@ -139,7 +139,7 @@ __global__ __launch_bounds__(kThreads) void fwd_f32_kernel(F32Params p) {
     }
   }
 
-  // Merge the four waves' partials: each writes (m, l, acc) to its region,
+  // Merge the waves' partials: each writes (m, l, acc) to its region,
   // then wave 0 combines them with weights exp(m_w - M).
   __syncthreads();
   {
