@@ -4,10 +4,14 @@
 // Decode is bound by reading the KV cache once per step ("Attention
 // Research", section 1; "Quadratic Complexity Bottleneck", KV cache entry).
 // Split-K over keys ("Attention Research", section 2) gives the GPU enough
-// independent work: the key range of each sequence (all Nk cache rows, or its
-// own length when lengths differ per sequence) is cut into S contiguous
-// chunks, and each (sequence, KV head, chunk) becomes one work-group that
-// reads its K/V rows exactly once for all G query heads sharing that KV head.
+// independent work. With equal lengths, each sequence's Nk cache rows are cut
+// into S contiguous chunks, and each (sequence, KV head, chunk) becomes one
+// work-group that reads its K/V rows exactly once for all G query heads
+// sharing that KV head. With per-sequence lengths, a small plan kernel lays
+// the visible keys of all sequences end to end in tiles, and each of the
+// B * S work-groups per KV head takes an equal run of whole tiles, cut at
+// sequence boundaries into pieces (one partial each), so a long sequence in a
+// batch of short ones is spread over the machine instead of over S chunks.
 //
 // A paged cache changes only where a key row is read from: row j of a
 // sequence lives in page block_table[b][j / page_size] of a page pool, at row
@@ -26,7 +30,8 @@
 // 32, one work-group each, which read the same keys. Each wave keeps its own
 // running max / sum / output; at the end the four waves are combined through
 // LDS into one normalised partial O_s and its lse_s = ln sum exp(scores) for
-// the chunk.
+// the chunk (a work-group whose run of tiles spans several sequences does
+// this once per piece).
 //
 // Merge kernel: per (sequence, query head), LSE = ln sum_s exp(lse_s) and
 // O = sum_s exp(lse_s - LSE) O_s; chunks with no visible key have
@@ -86,6 +91,11 @@ struct SplitParams {
   int window;
   float scale, scale_log2, thr_raw;
   const int* kv_lens;  // per-sequence key counts, or null (all Nk)
+  // Balanced pieces (per-sequence lengths): the plan written by
+  // decode_plan_kernel, tcum[0..B] = running sum of the sequences' visible
+  // tiles, tcum[B + 1] = tiles per work-group, tcum[B + 2 + w] = the sequence
+  // holding work-group w's first tile.
+  const int* tcum;
   // Paged cache: k, v are page pools [num_pages, Hkv, page_size, d] and
   // block_table [B, max_pages] names the physical page of each sequence's
   // j-th run of page_size keys (Nk = max_pages * page_size).
@@ -99,7 +109,14 @@ struct MergeParams {
   const float* lse_s;
   uint16_t* o;
   float* lse;
-  int BH, S;
+  int BH, S, H;
+  const int* tcum;  // balanced pieces: the plan (see SplitParams), else null
+};
+
+struct PlanParams {
+  const int* kv_lens;
+  int* tcum;
+  int B, Nk, window, W;
 };
 
 template <int D>
@@ -134,7 +151,7 @@ __device__ __forceinline__ int vswz(int r) {
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int D, bool PAGED>
+template <int D, bool PAGED, bool BAL>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p) {
   using T = DTile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[T::STAGE];
@@ -145,53 +162,87 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, g = lane >> 5;
-  // Grid order: split slowest. Consecutive work-groups are different
-  // (sequence, KV head, head block) units of the same split, so the XCDs,
-  // which receive work-groups round-robin, each get the same mix of chunk
-  // sizes (with per-sequence lengths, split s of every sequence in turn).
-  const int nbhb = p.B * p.Hkv * p.HB;
-  const int s = blockIdx.x / nbhb;
-  const int bhb = blockIdx.x - s * nbhb;
-  const int hb = bhb % p.HB;
-  const int bk = bhb / p.HB;
+
+  // The work of this work-group: (KV head, head block), and either
+  //  * equal chunks (!BAL): chunk s of sequence b, keys [s C, s C + C) with
+  //    C = ceil(n / S), or
+  //  * balanced pieces (BAL): the work-group's share [g_lo, g_hi) of the
+  //    batch's visible key tiles laid end to end (sequence b owns tiles
+  //    [Tc[b], Tc[b + 1]) of that list, starting at its first visible key),
+  //    cut at sequence boundaries into pieces; the piece of (work-group w,
+  //    sequence b) is partial w + b.
+  // Grid order: split (work-group share) slowest. Consecutive work-groups are
+  // different units of the same split, so the XCDs, which receive
+  // work-groups round-robin, each get the same mix of work.
+  const int nunit = BAL ? p.Hkv * p.HB : p.B * p.Hkv * p.HB;
+  const int s = blockIdx.x / nunit;
+  const int unit = blockIdx.x - s * nunit;
+  const int hb = unit % p.HB;
+  const int bk = unit / p.HB;
   const int g0 = hb * 32;               // first query head of this block in the group
   const int GB = min(32, p.G - g0);     // query heads in this block
-  const int kvh = bk % p.Hkv, b = bk / p.Hkv;
+  const int kvh = bk % p.Hkv;
 
-  // This sequence's keys (its first n cache rows; the query sits at n - 1),
-  // cut into S chunks of C = ceil(n / S); the window keeps the last W + 1.
-  const int n = p.kv_lens != nullptr ? min(max(p.kv_lens[b], 0), p.Nk) : p.Nk;
-  const int C = (n + p.S - 1) / p.S;
-  const int vis_lo = p.window > 0 ? max(0, n - 1 - p.window) : 0;
-  const int lo = min(n, s * C);
-  const int hi = min(n, lo + C);
-  const int start = max(lo, vis_lo);
-  const int ntiles = hi > start ? (hi - start + kBN - 1) / kBN : 0;
+  int b, start, hi, ntiles, g_lo = 0, g_hi = 0;
+  // Sequence b's keys: its first n cache rows (the query sits at n - 1); the
+  // window keeps the last W + 1.
+  auto seq_keys = [&](int bb, int& vis) -> int {
+    const int n = p.kv_lens != nullptr ? min(max(p.kv_lens[bb], 0), p.Nk) : p.Nk;
+    vis = p.window > 0 ? max(0, n - 1 - p.window) : 0;
+    return n;
+  };
+  // BAL: the piece of sequence b inside [g_lo, g_hi).
+  auto piece = [&]() {
+    int vis;
+    const int n = seq_keys(b, vis);
+    const int tb = p.tcum[b], tb1 = p.tcum[b + 1];
+    const int t_lo = max(tb, g_lo) - tb, t_hi = min(tb1, g_hi) - tb;
+    start = vis + t_lo * kBN;
+    hi = min(n, vis + t_hi * kBN);
+    ntiles = t_hi - t_lo;
+  };
+  if constexpr (BAL) {
+    const int total = p.tcum[p.B], budget = p.tcum[p.B + 1];
+    g_lo = s * budget;
+    if (g_lo >= total) return;  // the batch's tiles are all taken by earlier work-groups
+    g_hi = min(total, g_lo + budget);
+    b = p.tcum[p.B + 2 + s];    // the sequence that owns tile g_lo
+    piece();
+  } else {
+    b = bk / p.Hkv;
+    int vis;
+    const int n = seq_keys(b, vis);
+    const int C = (n + p.S - 1) / p.S;
+    const int lo = min(n, s * C);
+    hi = min(n, lo + C);
+    start = max(lo, vis);
+    ntiles = hi > start ? (hi - start + kBN - 1) / kBN : 0;
+  }
 
   // Query heads of this group as the B-operand columns.
   const bool qvalid = l32 < GB;
   const int hq = kvh * p.G + g0 + (qvalid ? l32 : 0);
   bf16x8 qf[T::KS];
-  {
+  auto load_q = [&]() {
     const uint16_t* qp = p.q + ((size_t)b * p.H + hq) * D + g * 8;
 #pragma unroll
     for (int ks = 0; ks < T::KS; ++ks) qf[ks] = as_bf16x8(load16(qp + ks * 16, qvalid));
-  }
+  };
+  load_q();
 
-  const size_t head_kv = ((size_t)b * p.Hkv + kvh) * p.Nk;
-  const int* table = PAGED ? p.block_table + (size_t)b * p.max_pages : nullptr;
   const int page_mask = (1 << p.page_shift) - 1;
   // Paged: thread tid < kBN reads the block-table entry of row t0 + tid (one
   // iteration before the rows themselves are loaded, so the table read is off
   // the load's critical path); rows past the chunk get -1.
   auto fetch_pid = [&](int t0) -> int {
     const int r = t0 + tid;
-    return (tid < kBN && r < hi) ? table[r >> p.page_shift] : -1;
+    return (tid < kBN && r < hi) ? p.block_table[(size_t)b * p.max_pages + (r >> p.page_shift)]
+                                 : -1;
   };
   // Element offset of cache row r (< hi) of tile t0 in page-id slot `slot`,
   // and whether it may be read: a page id outside the pool reads as zeros.
   auto row_at = [&](int r, int t0, int slot, bool& ok) -> size_t {
-    if (!PAGED) return (head_kv + (size_t)r) * D;
+    if (!PAGED) return (((size_t)b * p.Hkv + kvh) * p.Nk + (size_t)r) * D;
     const int pg = pid[slot][r - t0];
     ok = ok && (unsigned)pg < (unsigned)p.num_pages;
     const size_t page = ok ? (size_t)pg : 0;
@@ -248,130 +299,199 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
     }
   };
 
-  f32x16 oacc[T::DB];
-#pragma unroll
-  for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
-  float m_ref = -kInf;
-  float l_b = 0.f, l_f = 0.f;  // row sums of the bf16-rounded and the fp32 P
+  // Partial-result row of query head g0 + col of this chunk or piece.
+  auto prow = [&](int col) -> size_t {
+    const int h = kvh * p.G + g0 + col;
+    return BAL ? (size_t)(s + b) * p.H + h : ((size_t)b * p.H + h) * p.S + s;
+  };
 
-  int pid_next = -1;  // paged: page id of this thread's row of the tile after the next
-  if (ntiles > 0) {
-    if (PAGED) {
-      if (tid < kBN) pid[0][tid] = fetch_pid(start);
-      if (ntiles > 1) pid_next = fetch_pid(start + kBN);
+  for (;;) {
+    f32x16 oacc[T::DB];
+#pragma unroll
+    for (int i = 0; i < T::DB; ++i) oacc[i] = f32x16{};
+    float m_ref = -kInf;
+    float l_b = 0.f, l_f = 0.f;  // row sums of the bf16-rounded and the fp32 P
+
+    int pid_next = -1;  // paged: page id of this thread's row of the tile after the next
+    if (ntiles > 0) {
+      if (PAGED) {
+        if (tid < kBN) pid[0][tid] = fetch_pid(start);
+        if (ntiles > 1) pid_next = fetch_pid(start + kBN);
+        __syncthreads();
+      }
+      load_tile(start, 0);
+    }
+    for (int it = 0; it < ntiles; ++it) {
+      const int t0 = start + it * kBN;
+      __syncthreads();  // every wave is done with the previous tile
+      store_tile();
+      if (PAGED && tid < kBN) pid[(it + 1) & 1][tid] = pid_next;  // rows of tile it + 1
       __syncthreads();
+      if (it + 1 < ntiles) {
+        load_tile(t0 + kBN, (it + 1) & 1);
+        if (PAGED && it + 2 < ntiles) pid_next = fetch_pid(t0 + 2 * kBN);
+      }
+
+      const uint16_t* ks = smem;
+      const uint16_t* vs = smem + kBN * T::KSTR;
+      f32x16 sacc = f32x16{};
+      {
+        const uint16_t* kp = ks + (wave * 32 + l32) * T::KSTR + g * 8;
+#pragma unroll
+        for (int st = 0; st < T::KS; ++st) sacc = mfma32x32x16(lds_read_bf16x8(kp + st * 16), qf[st], sacc);
+      }
+      mfma_drain();
+      if (t0 + kBN > hi) {
+        const int lim = hi - (t0 + wave * 32 + 4 * g);  // offsets >= lim are past the chunk
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int c = 8 * (r >> 2) + (r & 3);
+          sacc[r] = c < lim ? sacc[r] : -kInf;
+        }
+      }
+      float mx = -kInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
+      mx = fmaxf(mx, swap_halves(mx));
+      const float m_new = fmaxf(m_ref, mx);
+      const bool need = m_new > m_ref + p.thr_raw;
+      if (wave_any(need)) {
+        const float alpha = need ? fast_exp2((m_ref - m_new) * p.scale_log2) : 1.f;
+        if (need) m_ref = m_new;
+        l_b *= alpha;
+        l_f *= alpha;
+#pragma unroll
+        for (int i = 0; i < T::DB; ++i) oacc[i] *= alpha;
+      }
+      const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
+      bf16x8 pf[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        f32x8 pv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+          pv[i] = fast_exp2(__builtin_fmaf(sacc[hf * 8 + i], p.scale_log2, -msub));
+        l_f += sum_f32x8(pv);
+        pf[hf] = to_bf16x8(pv);
+        l_b = sum_bf16x8(pf[hf], l_b);
+      }
+      const lds_u8* vl = lds_ptr((void*)vs) + wave * 32 * T::VROWB;  // this wave's 32 keys
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int db = 0; db < T::DB; ++db) {
+          const uint2 lo = lds_tr_b64(vl, voff[db][0] + t * 16 * T::VROWB);
+          const uint2 hi2 = lds_tr_b64(vl, voff[db][1] + t * 16 * T::VROWB);
+          const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi2.x, hi2.y));
+          oacc[db] = mfma32x32x16(va, pf[t], oacc[db]);
+        }
+      mfma_drain();
     }
-    load_tile(start, 0);
-  }
-  for (int it = 0; it < ntiles; ++it) {
-    const int t0 = start + it * kBN;
-    __syncthreads();  // every wave is done with the previous tile
-    store_tile();
-    if (PAGED && tid < kBN) pid[(it + 1) & 1][tid] = pid_next;  // rows of tile it + 1
+
+    // Combine the four waves' (max, sum, un-normalised output) per head.
+    const float lb_col = l_b + swap_halves(l_b);
+    const float lf_col = l_f + swap_halves(l_f);
+    __syncthreads();  // tile storage is free again
+    float* ow = reinterpret_cast<float*>(smem);   // [4][32][D]
+    float* mw = ow + 4 * 32 * D;                  // [4][32]
+    float* lbw = mw + 4 * 32;                     // [4][32] sums of rounded P
+    float* lfw = lbw + 4 * 32;                    // [4][32] sums of fp32 P
+    if (qvalid) {
+      float* dst = ow + (wave * 32 + l32) * D + 4 * g;
+#pragma unroll
+      for (int db = 0; db < T::DB; ++db)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          *reinterpret_cast<f32x4*>(dst + db * 32 + rr * 8) =
+              f32x4{oacc[db][rr * 4], oacc[db][rr * 4 + 1], oacc[db][rr * 4 + 2], oacc[db][rr * 4 + 3]};
+      if (g == 0) {
+        mw[wave * 32 + l32] = m_ref;
+        lbw[wave * 32 + l32] = lb_col;
+        lfw[wave * 32 + l32] = lf_col;
+      }
+    }
     __syncthreads();
-    if (it + 1 < ntiles) {
-      load_tile(t0 + kBN, (it + 1) & 1);
-      if (PAGED && it + 2 < ntiles) pid_next = fetch_pid(t0 + 2 * kBN);
+    for (int idx = tid; idx < GB * D; idx += kThreads) {
+      const int col = idx / D, dim = idx - col * D;
+      float M = -kInf;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) M = fmaxf(M, mw[w * 32 + col]);
+      float Lb = 0.f, Lf = 0.f, acc = 0.f;
+      if (M != -kInf) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const float mwv = mw[w * 32 + col];
+          const float e = mwv == -kInf ? 0.f : fast_exp2((mwv - M) * p.scale_log2);
+          Lb += e * lbw[w * 32 + col];
+          Lf += e * lfw[w * 32 + col];
+          acc += e * ow[(w * 32 + col) * D + dim];
+        }
+      }
+      const size_t row = prow(col);
+      p.o_s[row * D + dim] = Lb > 0.f ? acc / Lb : 0.f;
+      if (dim == 0) p.lse_s[row] = Lf > 0.f ? M * p.scale + fast_log2(Lf) * kLn2 : -kInf;
     }
 
-    const uint16_t* ks = smem;
-    const uint16_t* vs = smem + kBN * T::KSTR;
-    f32x16 sacc = f32x16{};
-    {
-      const uint16_t* kp = ks + (wave * 32 + l32) * T::KSTR + g * 8;
-#pragma unroll
-      for (int st = 0; st < T::KS; ++st) sacc = mfma32x32x16(lds_read_bf16x8(kp + st * 16), qf[st], sacc);
+    if constexpr (!BAL) {
+      break;
+    } else {
+      if (p.tcum[b + 1] >= g_hi) break;
+      // The next sequence that owns tiles (one does: this share goes on).
+      do {
+        ++b;
+      } while (p.tcum[b + 1] == p.tcum[b]);
+      piece();
+      load_q();
     }
-    mfma_drain();
-    if (t0 + kBN > hi) {
-      const int lim = hi - (t0 + wave * 32 + 4 * g);  // offsets >= lim are past the chunk
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = 8 * (r >> 2) + (r & 3);
-        sacc[r] = c < lim ? sacc[r] : -kInf;
-      }
-    }
-    float mx = -kInf;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[r]);
-    mx = fmaxf(mx, swap_halves(mx));
-    const float m_new = fmaxf(m_ref, mx);
-    const bool need = m_new > m_ref + p.thr_raw;
-    if (wave_any(need)) {
-      const float alpha = need ? fast_exp2((m_ref - m_new) * p.scale_log2) : 1.f;
-      if (need) m_ref = m_new;
-      l_b *= alpha;
-      l_f *= alpha;
-#pragma unroll
-      for (int i = 0; i < T::DB; ++i) oacc[i] *= alpha;
-    }
-    const float msub = (m_ref == -kInf) ? 0.f : m_ref * p.scale_log2;
-    bf16x8 pf[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      f32x8 pv;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        pv[i] = fast_exp2(__builtin_fmaf(sacc[hf * 8 + i], p.scale_log2, -msub));
-      l_f += sum_f32x8(pv);
-      pf[hf] = to_bf16x8(pv);
-      l_b = sum_bf16x8(pf[hf], l_b);
-    }
-    const lds_u8* vl = lds_ptr((void*)vs) + wave * 32 * T::VROWB;  // this wave's 32 keys
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int db = 0; db < T::DB; ++db) {
-        const uint2 lo = lds_tr_b64(vl, voff[db][0] + t * 16 * T::VROWB);
-        const uint2 hi2 = lds_tr_b64(vl, voff[db][1] + t * 16 * T::VROWB);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, make_uint4(lo.x, lo.y, hi2.x, hi2.y));
-        oacc[db] = mfma32x32x16(va, pf[t], oacc[db]);
-      }
-    mfma_drain();
   }
+}
 
-  // Combine the four waves' (max, sum, un-normalised output) per head.
-  const float lb_col = l_b + swap_halves(l_b);
-  const float lf_col = l_f + swap_halves(l_f);
-  __syncthreads();  // tile storage is free again
-  float* ow = reinterpret_cast<float*>(smem);   // [4][32][D]
-  float* mw = ow + 4 * 32 * D;                  // [4][32]
-  float* lbw = mw + 4 * 32;                     // [4][32] sums of rounded P
-  float* lfw = lbw + 4 * 32;                    // [4][32] sums of fp32 P
-  if (qvalid) {
-    float* dst = ow + (wave * 32 + l32) * D + 4 * g;
-#pragma unroll
-    for (int db = 0; db < T::DB; ++db)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-        *reinterpret_cast<f32x4*>(dst + db * 32 + rr * 8) =
-            f32x4{oacc[db][rr * 4], oacc[db][rr * 4 + 1], oacc[db][rr * 4 + 2], oacc[db][rr * 4 + 3]};
-    if (g == 0) {
-      mw[wave * 32 + l32] = m_ref;
-      lbw[wave * 32 + l32] = lb_col;
-      lfw[wave * 32 + l32] = lf_col;
+// Plan of the balanced pieces (one work-group): sequence b owns
+// t_b = ceil((n_b - vis_b) / kBN) tiles of the batch's visible keys; tcum is
+// their running sum, every work-group of the split grid takes
+// ceil(total / W) consecutive tiles of that list, and for each work-group
+// that gets any, the sequence holding its first tile is recorded.
+__global__ __launch_bounds__(kThreads) void decode_plan_kernel(PlanParams p) {
+  __shared__ int wsum[kThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int carry = 0;
+  for (int base = 0; base < p.B; base += kThreads) {
+    const int b = base + tid;
+    int t = 0;
+    if (b < p.B) {
+      const int n = min(max(p.kv_lens[b], 0), p.Nk);
+      const int vis = p.window > 0 ? max(0, n - 1 - p.window) : 0;
+      t = (n - vis + kBN - 1) / kBN;
     }
+    int x = t;  // inclusive running sum within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(x, off, 64);
+      if (lane >= off) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = carry, all = 0;
+#pragma unroll
+    for (int w = 0; w < kThreads / 64; ++w) {
+      before += w < wave ? wsum[w] : 0;
+      all += wsum[w];
+    }
+    if (b < p.B) p.tcum[b] = before + x - t;
+    carry += all;
+    __syncthreads();  // wsum is rewritten by the next round
   }
-  __syncthreads();
-  for (int idx = tid; idx < GB * D; idx += kThreads) {
-    const int col = idx / D, dim = idx - col * D;
-    float M = -kInf;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, mw[w * 32 + col]);
-    float Lb = 0.f, Lf = 0.f, acc = 0.f;
-    if (M != -kInf) {
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const float mwv = mw[w * 32 + col];
-        const float e = mwv == -kInf ? 0.f : fast_exp2((mwv - M) * p.scale_log2);
-        Lb += e * lbw[w * 32 + col];
-        Lf += e * lfw[w * 32 + col];
-        acc += e * ow[(w * 32 + col) * D + dim];
-      }
-    }
-    const size_t row = ((size_t)b * p.H + kvh * p.G + g0 + col) * p.S + s;
-    p.o_s[row * D + dim] = Lb > 0.f ? acc / Lb : 0.f;
-    if (dim == 0) p.lse_s[row] = Lf > 0.f ? M * p.scale + fast_log2(Lf) * kLn2 : -kInf;
+  const int total = carry;
+  const int budget = max(1, (total + p.W - 1) / p.W);
+  if (tid == 0) {
+    p.tcum[p.B] = total;
+    p.tcum[p.B + 1] = budget;
+  }
+  __syncthreads();  // every running sum is written
+  for (int b = tid; b < p.B; b += kThreads) {
+    const int tb = p.tcum[b], tb1 = b + 1 < p.B ? p.tcum[b + 1] : total;
+    // Work-groups whose first tile w * budget lies in [tb, tb1).
+    for (int w = (tb + budget - 1) / budget; w * budget < tb1; ++w) p.tcum[p.B + 2 + w] = b;
   }
 }
 
@@ -380,22 +500,36 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
   constexpr int DPL = D / 64;  // dims per lane
   const int lane = threadIdx.x;
   const int bh = blockIdx.x;
-  const float* ls = p.lse_s + (size_t)bh * p.S;
-  const float* os = p.o_s + (size_t)bh * p.S * D;
+  // This (sequence, head)'s partials: rows first + i * stride, i < count.
+  size_t first = (size_t)bh * p.S, stride = 1;
+  int count = p.S;
+  if (p.tcum != nullptr) {
+    // Balanced pieces: work-groups w_lo .. w_hi hold sequence b's tiles, and
+    // the piece of (w, b) is partial w + b.
+    const int b = bh / p.H, h = bh - b * p.H;
+    const int tb = p.tcum[b], tb1 = p.tcum[b + 1], budget = p.tcum[p.BH / p.H + 1];
+    const int w_lo = tb / budget;
+    count = tb1 > tb ? (tb1 - 1) / budget - w_lo + 1 : 0;
+    first = (size_t)(w_lo + b) * p.H + h;
+    stride = p.H;
+  }
+  const float* ls = p.lse_s;
+  const float* os = p.o_s;
   float M = -kInf;
-  for (int s = lane; s < p.S; s += 64) M = fmaxf(M, ls[s]);
+  for (int s = lane; s < count; s += 64) M = fmaxf(M, ls[first + s * stride]);
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w, 64));
   float L = 0.f, acc[DPL];
 #pragma unroll
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   if (M != -kInf) {
-    for (int s = 0; s < p.S; ++s) {
-      const float lv = ls[s];
+    for (int s = 0; s < count; ++s) {
+      const size_t row = first + s * stride;
+      const float lv = ls[row];
       const float w = lv == -kInf ? 0.f : expf(lv - M);
       L += w;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(w, os[(size_t)s * D + lane * DPL + i], acc[i]);
+      for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(w, os[row * D + lane * DPL + i], acc[i]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -411,8 +545,12 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
 
 }  // namespace
 
+// Partial rows: B * H * S for equal chunks; with balanced pieces, one per
+// (work-group share w < B * S, sequence b) pair that can occur, indexed
+// w + b < B * (S + 1), per query head. Then the plan: B + 2 + B * S ints.
 size_t decode_workspace_bytes(int B, int H, int d, int splits) {
-  return (size_t)B * H * splits * (size_t)(d + 1) * sizeof(float);
+  const size_t rows = (size_t)B * H * (splits + 1);
+  return rows * (size_t)(d + 1) * sizeof(float) + ((size_t)B * (splits + 1) + 2) * sizeof(int);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
@@ -420,8 +558,14 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.q = static_cast<const uint16_t*>(a.q);
   sp.k = static_cast<const uint16_t*>(a.k);
   sp.v = static_cast<const uint16_t*>(a.v);
+  const size_t rows = (size_t)a.B * a.H * (a.splits + 1);
   sp.o_s = static_cast<float*>(a.workspace);
-  sp.lse_s = sp.o_s + (size_t)a.B * a.H * a.splits * a.d;
+  sp.lse_s = sp.o_s + rows * a.d;
+  int* plan = reinterpret_cast<int*>(sp.lse_s + rows);
+  // Per-sequence lengths (and paged caches, which always have them) use
+  // balanced pieces; equal lengths keep one equal chunk per work-group.
+  const bool bal = a.kv_lens != nullptr;
+  sp.tcum = bal ? plan : nullptr;
   sp.B = a.B;
   sp.H = a.H;
   sp.Hkv = a.Hkv;
@@ -439,21 +583,34 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.scale = a.scale;
   sp.scale_log2 = a.scale * kLog2e;
   sp.thr_raw = kRescaleThreshold / sp.scale_log2;
+  // Both layouts launch B * S work-groups per (KV head, head block).
   const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * sp.HB * a.splits);
   if (log_enabled())
     fprintf(stderr,
             "[miattn] decode d=%d splits=%d kv_lens=%s page_size=%d split_grid=%u "
             "merge_grid=%d\n",
-            a.d, a.splits, a.kv_lens != nullptr ? "per-sequence" : "uniform",
+            a.d, a.splits, bal ? "per-sequence (balanced pieces)" : "uniform",
             a.block_table != nullptr ? a.page_size : 0, nsplit_blk, a.B * a.H);
+  hipError_t e;
+  if (bal) {
+    PlanParams pp{a.kv_lens, plan, a.B, a.Nk, a.window, a.B * a.splits};
+    void* pargs[] = {&pp};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_plan_kernel), dim3(1),
+                        dim3(kThreads), pargs, 0, stream);
+    if (e != hipSuccess) return e;
+  }
   void* sargs[] = {&sp};
   const bool paged = a.block_table != nullptr;
-  const void* sfn =
-      a.d == 128 ? (paged ? reinterpret_cast<const void*>(&decode_split_kernel<128, true>)
-                          : reinterpret_cast<const void*>(&decode_split_kernel<128, false>))
-                 : (paged ? reinterpret_cast<const void*>(&decode_split_kernel<64, true>)
-                          : reinterpret_cast<const void*>(&decode_split_kernel<64, false>));
-  hipError_t e = hipLaunchKernel(sfn, dim3(nsplit_blk), dim3(kThreads), sargs, 0, stream);
+  const void* sfn;
+  if (a.d == 128)
+    sfn = paged ? reinterpret_cast<const void*>(&decode_split_kernel<128, true, true>)
+          : bal ? reinterpret_cast<const void*>(&decode_split_kernel<128, false, true>)
+                : reinterpret_cast<const void*>(&decode_split_kernel<128, false, false>);
+  else
+    sfn = paged ? reinterpret_cast<const void*>(&decode_split_kernel<64, true, true>)
+          : bal ? reinterpret_cast<const void*>(&decode_split_kernel<64, false, true>)
+                : reinterpret_cast<const void*>(&decode_split_kernel<64, false, false>);
+  e = hipLaunchKernel(sfn, dim3(nsplit_blk), dim3(kThreads), sargs, 0, stream);
   if (e != hipSuccess) return e;
 
   MergeParams mp;
@@ -463,6 +620,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   mp.lse = a.lse;
   mp.BH = a.B * a.H;
   mp.S = a.splits;
+  mp.H = a.H;
+  mp.tcum = sp.tcum;
   void* margs[] = {&mp};
   const void* mfn = a.d == 128 ? reinterpret_cast<const void*>(&decode_merge_kernel<128>)
                                : reinterpret_cast<const void*>(&decode_merge_kernel<64>);

@@ -149,6 +149,11 @@ int run_decode(const void* q, const void* k_cache, const void* v_cache, const in
   const long long hb = (H / Hkv + 31) / 32;  // blocks of 32 query heads per K/V head
   if ((long long)B * Hkv * hb * S > (long long)INT_MAX || (long long)B * H > (long long)INT_MAX)
     return MIATTN_EUNSUPPORTED;
+  // Per-sequence lengths: partial rows are indexed by (share + sequence) <
+  // B (S + 1), and the plan counts the batch's key tiles in int.
+  if (kv_lens != nullptr && ((long long)B * (S + 1) > (long long)INT_MAX ||
+                             (long long)B * ((Nk + 127) / 128) > (long long)INT_MAX / 2))
+    return MIATTN_EUNSUPPORTED;
   if (B == 0) return MIATTN_OK;
   if (q == nullptr || o == nullptr) return MIATTN_EINVAL;
   const bool paged = block_table != nullptr;

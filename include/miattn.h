@@ -219,9 +219,12 @@ int attn_bwd_varlen(const void* q, const void* k, const void* v, const void* o,
  * groups of more than 32 query heads are processed in blocks of 32 (each
  * block reads the group's keys).
  *
- * attn_decode_workspace_bytes returns B * H * S * (d + 1) * 4 bytes: the fp32
- * partial outputs O_s [B, H, S, d] followed by lse_s [B, H, S], where S is
- * the split count the decode call will use. It takes Hkv and Nk (and not only
+ * attn_decode_workspace_bytes returns B * H * (S + 1) * (d + 1) * 4 +
+ * (B * (S + 1) + 2) * 4 bytes, where S is the split count the decode call
+ * will use: room for the fp32 partial outputs O_s and their lse_s (B * H * S
+ * of each here; up to B * H * (S + 1) for the per-sequence-length and paged
+ * variants below), then the int32 work plan those variants build. The
+ * contents are the library's own between calls. It takes Hkv and Nk (and not only
  * B, H, d and num_splits) because num_splits = 0 means "library's choice",
  * which depends on the number of (sequence, KV head) units B * Hkv and on the
  * key count Nk (attn_decode_num_splits); with the same arguments as the
@@ -264,12 +267,19 @@ int attn_decode_splitk_noalloc(const void* q, const void* k_cache, const void* v
 /*
  * Split-K decode over caches whose sequences hold different numbers of keys.
  * Sequence b uses the first kv_lens[b] rows of its [Hkv, Nk, d] cache slot;
- * its query sits at position kv_lens[b] - 1. Each sequence's own key range is
- * cut into num_splits chunks of ceil(kv_lens[b] / num_splits) keys, so work
- * follows the real lengths. kv_lens: DEVICE int32 [B]; values are clamped to
- * [0, Nk], and a sequence of length 0 gets O = 0, LSE = -inf. Everything else
- * (layout, workspace size, split count, errors) is as for attn_decode_splitk;
- * kv_lens must be non-NULL when B > 0.
+ * its query sits at position kv_lens[b] - 1. The work follows the real
+ * lengths and is balanced over the batch: the visible keys of all sequences
+ * are laid end to end in tiles of 128 (each sequence's run starting at its
+ * first visible key), and each of the B * num_splits work-groups per KV head
+ * takes an equal run of whole tiles, cut at sequence boundaries into pieces
+ * that each yield one partial (O_s, lse_s) of one sequence; the merge then
+ * combines a sequence's pieces as above. A small first kernel builds this
+ * plan from kv_lens on the device, so the call needs no host copy of the
+ * lengths. kv_lens: DEVICE int32 [B]; values are clamped to [0, Nk], and a
+ * sequence of length 0 gets O = 0, LSE = -inf. Everything else (layout,
+ * workspace size, split count, errors) is as for attn_decode_splitk; kv_lens
+ * must be non-NULL when B > 0, and B * (num_splits + 1) and twice the batch's
+ * tile count B * ceil(Nk / 128) must fit in an int (else MIATTN_EUNSUPPORTED).
  */
 int attn_decode_splitk_varlen(const void* q, const void* k_cache, const void* v_cache,
                               const int* kv_lens, void* o, float* lse,

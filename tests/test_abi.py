@@ -118,10 +118,12 @@ def test_decode_split_resolution_and_workspace(lib):
     auto = lib.attn_decode_num_splits(64, 8, 32768, 0)
     assert 1 <= auto <= 32768
     assert lib.attn_decode_num_splits(1, 1, 0, 0) == 1
-    # O_s fp32 [B, H, S, d] then lse_s fp32 [B, H, S]
-    assert lib.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 16) == 64 * 32 * 16 * 129 * 4
+    # fp32 O_s and lse_s for up to B * H * (S + 1) partials, then B * (S + 1) + 2 plan ints
+    assert (lib.attn_decode_workspace_bytes(64, 32, 8, 32768, 128, 16)
+            == 64 * 32 * 17 * 129 * 4 + (64 * 17 + 2) * 4)
     s = lib.attn_decode_num_splits(3, 2, 1000, 0)
-    assert lib.attn_decode_workspace_bytes(3, 8, 2, 1000, 64, 0) == 3 * 8 * s * 65 * 4
+    assert (lib.attn_decode_workspace_bytes(3, 8, 2, 1000, 64, 0)
+            == 3 * 8 * (s + 1) * 65 * 4 + (3 * (s + 1) + 2) * 4)
 
 
 def dec(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=FAKE, B=2, H=8, Hkv=2, Nk=100, d=128,

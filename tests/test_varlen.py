@@ -9,8 +9,9 @@ fixed-length kernel bit for bit. (The packed workload at full size is
 compared on every output in test_full_size.py.)
 
 Decode (attn_decode_varlen): parity on mixed lengths including 0 and 1;
-cache rows past a sequence's length never matter; full-length sequences
-equal attn_decode bit for bit; each sequence equals a one-query packed
+work-group runs of tiles that cross sequences, or find none; cache rows past
+a sequence's length never matter; full-length sequences equal attn_decode
+bit for bit where its equal chunks are whole tiles; each sequence equals a one-query packed
 prefill over its keys. (The mixed-length workload at full size is compared on
 every output in test_full_size.py.)
 """
@@ -226,6 +227,36 @@ def test_decode_varlen_parity(d, splits, window):
     assert torch.all(o[0] == 0) and torch.all(torch.isneginf(lse[0]))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("splits,window", [(1, 0), (2, 0), (16, 0), (3, 50)])
+def test_decode_varlen_pieces_span_sequences(d, splits, window):
+    """Many short and empty sequences (23 key tiles in all, 16 sequences): with one split a
+    work-group's run of tiles crosses several sequences; with 16 splits most of the 256
+    work-groups per KV head get no tile at all."""
+    lens = [0, 1, 5, 127, 128, 129, 0, 300, 2, 64, 1000, 0, 3, 256, 17, 0]
+    q, kc, vc = decode_case(len(lens), 8, 2, 1000, d, seed=11 + d)
+    o, lse = run_decode(q, kc, vc, lens, 0.088, window, splits)
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.088, window)
+    label = f"d={d} splits={splits} W={window}"
+    check_out(to64(o), o_ref, label=label)
+    check_lse(to64(lse), l_ref, label=label)
+    for b, n in enumerate(lens):
+        if n == 0:
+            assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b]))
+
+
+def test_decode_varlen_skewed_batch():
+    """One long sequence among one-key ones (157 + 31 tiles for 512 work-groups per KV head):
+    each work-group takes one tile, so the long sequence's keys come back as 157 partials,
+    which the merge combines over three rounds of its 64 lanes."""
+    lens = [20000] + [1] * 31
+    q, kc, vc = decode_case(len(lens), 8, 2, 20000, 128, seed=12)
+    o, lse = run_decode(q, kc, vc, lens, 0.088, 0, 16)
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.088, 0)
+    check_out(to64(o), o_ref, label="skewed")
+    check_lse(to64(lse), l_ref, label="skewed")
+
+
 @pytest.mark.parametrize("H,Hkv", [(40, 1), (64, 1)])
 def test_decode_varlen_many_heads_per_group(H, Hkv):
     lens = [0, 1, 200, 333]
@@ -248,10 +279,13 @@ def test_decode_varlen_ignores_rows_past_length():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("splits", [1, 5, 16])
-def test_decode_varlen_full_lengths_match_uniform_kernel(splits):
-    q, kc, vc = decode_case(3, 32, 8, 777, 128, seed=4)
-    o1, l1 = run_decode(q, kc, vc, [777] * 3, 0.088, 0, splits)
+@pytest.mark.parametrize("Nk,splits", [(777, 1), (1280, 5), (2048, 16), (4096, 8)])
+def test_decode_varlen_full_lengths_match_uniform_kernel(Nk, splits):
+    """All lengths equal to Nk, with each of the S equal chunks a whole number of 128-key
+    tiles (or one chunk per sequence): the balanced pieces of the per-sequence-length kernel
+    are then exactly the equal chunks, merged in the same order, so the two agree bit for bit."""
+    q, kc, vc = decode_case(3, 32, 8, Nk, 128, seed=4)
+    o1, l1 = run_decode(q, kc, vc, [Nk] * 3, 0.088, 0, splits)
     o2, l2 = mi.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), scale=0.088, num_splits=splits)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)

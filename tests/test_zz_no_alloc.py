@@ -91,16 +91,20 @@ def test_noalloc_library_split_choice_and_binding(lib):
 
 
 def test_noalloc_refuses_requests_past_the_scratch(lib):
-    # 64 x 32 heads x 64 splits x 129 x 4 B = 67.6 MB of partials > 32 MiB
+    # 64 x 32 heads x 65 x 129 x 4 B = 68.7 MB of partials > 32 MiB
     B, H, Hkv, Nk, d, S = 64, 32, 8, 32768, 128, 64
-    assert B * H * S * (d + 1) * 4 > SCRATCH_BYTES
+    assert lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, S) > SCRATCH_BYTES
     st = lib.attn_decode_splitk_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, B, H, Hkv, Nk, d,
                                         ctypes.c_float(0.088), 0, S, None)
     assert st == MIATTN_ESCRATCH
     assert "scratch" in lib.attn_strerror(st).decode()
-    # just under the limit is accepted by validation (it then needs a device)
-    S_ok = SCRATCH_BYTES // (B * H * (d + 1) * 4)
-    assert lib.attn_decode_num_splits(B, Hkv, Nk, S_ok) == S_ok
+    # the largest split count whose partials fit, and the first that does not
+    S_ok = max(s for s in range(1, S) if lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, s)
+               <= SCRATCH_BYTES)
+    assert lib.attn_decode_workspace_bytes(B, H, Hkv, Nk, d, S_ok + 1) > SCRATCH_BYTES
+    over = lib.attn_decode_splitk_noalloc(FAKE, FAKE, FAKE, FAKE, FAKE, B, H, Hkv, Nk, d,
+                                          ctypes.c_float(0.088), 0, S_ok + 1, None)
+    assert over == MIATTN_ESCRATCH
 
 
 def test_noalloc_argument_errors(lib):
