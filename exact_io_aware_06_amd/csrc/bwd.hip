@@ -8,11 +8,12 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dQ = scale dS K,
 //   dK = scale dS^T Q.
 //
-// Four kernels, no atomics (every output element has exactly one writer, so
+// Three kernels, no atomics (every output element has exactly one writer, so
 // results are deterministic):
-//   bwd_prep  D for every query row (reads dO and O once).
 //   bwd_dq    one work-group per (batch, head, 128 query rows), four waves of
-//             32 rows, streaming the visible 64-key K/V tiles through LDS:
+//             32 rows; first D of its rows (from its dO and the stored O),
+//             which it also publishes with the exp2-domain LSE for bwd_dkdv;
+//             then, streaming the visible 64-key K/V tiles through LDS:
 //             S^T = K Q^T and dP^T = V dO^T on matrix cores (Q, dO stay in
 //             registers), dS^T on the vector ALU, then dQ^T += K^T dS^T with
 //             dS^T straight from registers and K^T gathered by transposing LDS
@@ -171,33 +172,6 @@ __device__ __forceinline__ Rows rows_of(const BwdParams& p, int b, int h, int kv
 }
 
 // ---------------------------------------------------------------------------
-// D = rowsum(dO * O), fp32, over the stored (bf16) O; and the LSE in the
-// exp2 domain, with +inf for rows that see no key (so P = 0 on every masked
-// or unmasked score of such a row, with no inf - inf).
-
-template <int D>
-__global__ __launch_bounds__(kThreads) void bwd_prep_kernel(BwdParams p, long long rows) {
-  constexpr int TPR = D / 8;  // lanes per row, 8 elements each
-  constexpr int RPB = kThreads / TPR;
-  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
-  const int c = (threadIdx.x % TPR) * 8;
-  const bool ok = row < rows;
-  const uint4 a = load16(p.dout + (ok ? row : 0) * D + c, ok);
-  const uint4 b = load16(p.o + (ok ? row : 0) * D + c, ok);
-  const bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) s = __builtin_fmaf((float)x[i], (float)y[i], s);
-#pragma unroll
-  for (int w = TPR / 2; w >= 1; w >>= 1) s += __shfl_xor(s, w, 64);
-  if (ok && threadIdx.x % TPR == 0) {
-    p.delta[row] = s;
-    const float l = p.lse[row];
-    p.lse2[row] = l == -kInf ? kInf : l * kLog2e;
-  }
-}
-
-// ---------------------------------------------------------------------------
 // dQ.
 
 template <int D>
@@ -260,19 +234,33 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   const size_t head_q = R.head_q;
 
   bf16x8 qf[KS], df[KS];
+  float dlt = 0.f;  // D = rowsum(dO * O) of this row, fp32 over the stored bf16 O
   {
     const size_t r = (head_q + (qvalid ? qrow : 0)) * D + g * 8;
+    bf16x8 of[KS];
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
       qf[ks] = as_bf16x8(load16(p.q + r + ks * 16, qvalid));
       df[ks] = as_bf16x8(load16(p.dout + r + ks * 16, qvalid));
+      of[ks] = as_bf16x8(load16(p.o + r + ks * 16, qvalid));
     }
+    // This lane holds half of the row's dims (chunks g, g + 2, ...), lane
+    // l32 + 32 the other half.
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dlt = __builtin_fmaf((float)df[ks][i], (float)of[ks][i], dlt);
+    dlt += swap_halves(dlt);
   }
   // exp2-domain LSE of this row (+inf for a row that sees no key, so every
-  // P of it is 0) and its D.
+  // P of it is 0). It and D are published for the dK / dV pass, which reads
+  // them for rows of its documents only, all of which have a dQ work-group.
   const float lse_row = qvalid ? p.lse[head_q + qrow] : -kInf;
   const float lse2 = lse_row == -kInf ? kInf : lse_row * kLog2e;
-  const float dlt = qvalid ? p.delta[head_q + qrow] : 0.f;
+  if (qvalid && g == 0) {
+    p.delta[head_q + qrow] = dlt;
+    p.lse2[head_q + qrow] = lse2;
+  }
 
   LOffsets<D> lo;
   lo.init(lane);
@@ -800,11 +788,7 @@ hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
   const long long nb = prm.cu_q != nullptr ? 1 : prm.B;
   const long long rows = nb * prm.H * prm.Nq;
   if (rows > 0) {
-    constexpr int RPB = kThreads / (D / 8);
-    void* pargs[] = {&prm, const_cast<long long*>(&rows)};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_prep_kernel<D>),
-                        dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(kThreads), pargs, 0, stream);
-    if (e != hipSuccess) return e;
+    // also writes D and the exp2-domain LSE of every row for the dK / dV pass
     e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dq_kernel<D>),
                         dim3((unsigned)((size_t)prm.B * prm.H * prm.nqt)), dim3(kThreads), args,
                         0, stream);
