@@ -245,6 +245,19 @@ def test_decode_varlen_pieces_span_sequences(d, splits, window):
             assert torch.all(o[b] == 0) and torch.all(torch.isneginf(lse[b]))
 
 
+def test_decode_varlen_large_batch():
+    """300 sequences: the plan's running sum over the batch takes two rounds of its 256
+    threads."""
+    rng = np.random.default_rng(13)
+    lens = rng.integers(0, 301, size=300).tolist()
+    lens[:3] = [0, 300, 1]
+    q, kc, vc = decode_case(len(lens), 4, 1, 300, 64, seed=13)
+    o, lse = run_decode(q, kc, vc, lens, 0.125, 0, 2)
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.125, 0)
+    check_out(to64(o), o_ref, label="B=300")
+    check_lse(to64(lse), l_ref, label="B=300")
+
+
 def test_decode_varlen_skewed_batch():
     """One long sequence among one-key ones (157 + 31 tiles for 512 work-groups per KV head):
     each work-group takes one tile, so the long sequence's keys come back as 157 partials,
