@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   //    batch's visible key tiles laid end to end (sequence b owns tiles
   //    [Tc[b], Tc[b + 1]) of that list, starting at its first visible key),
   //    cut at sequence boundaries into pieces; the piece of (work-group w,
-  //    sequence b) is partial w + b.
+  //    sequence b) is partial w + b among each query head's B (S + 1) rows.
   // Grid order: split (work-group share) slowest. Consecutive work-groups are
   // different units of the same split, so the XCDs, which receive
   // work-groups round-robin, each get the same mix of work.
@@ -302,7 +302,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   // Partial-result row of query head g0 + col of this chunk or piece.
   auto prow = [&](int col) -> size_t {
     const int h = kvh * p.G + g0 + col;
-    return BAL ? (size_t)(s + b) * p.H + h : ((size_t)b * p.H + h) * p.S + s;
+    // Balanced pieces: head-major, so that one sequence's pieces are adjacent rows.
+    return BAL ? (size_t)h * ((size_t)p.B * (p.S + 1)) + s + b : ((size_t)b * p.H + h) * p.S + s;
   };
 
   for (;;) {
@@ -500,23 +501,22 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
   constexpr int DPL = D / 64;  // dims per lane
   const int lane = threadIdx.x;
   const int bh = blockIdx.x;
-  // This (sequence, head)'s partials: rows first + i * stride, i < count.
-  size_t first = (size_t)bh * p.S, stride = 1;
+  // This (sequence, head)'s partials: rows first .. first + count - 1.
+  size_t first = (size_t)bh * p.S;
   int count = p.S;
   if (p.tcum != nullptr) {
     // Balanced pieces: work-groups w_lo .. w_hi hold sequence b's tiles, and
-    // the piece of (w, b) is partial w + b.
+    // the piece of (w, b) is partial w + b of head h's B (S + 1) rows.
     const int b = bh / p.H, h = bh - b * p.H;
     const int tb = p.tcum[b], tb1 = p.tcum[b + 1], budget = p.tcum[p.BH / p.H + 1];
     const int w_lo = tb / budget;
     count = tb1 > tb ? (tb1 - 1) / budget - w_lo + 1 : 0;
-    first = (size_t)(w_lo + b) * p.H + h;
-    stride = p.H;
+    first = (size_t)h * ((size_t)(p.BH / p.H) * (p.S + 1)) + w_lo + b;  // head-major rows
   }
   const float* ls = p.lse_s;
   const float* os = p.o_s;
   float M = -kInf;
-  for (int s = lane; s < count; s += 64) M = fmaxf(M, ls[first + s * stride]);
+  for (int s = lane; s < count; s += 64) M = fmaxf(M, ls[first + s]);
 #pragma unroll
   for (int w = 32; w >= 1; w >>= 1) M = fmaxf(M, __shfl_xor(M, w, 64));
   float L = 0.f, acc[DPL];
@@ -524,7 +524,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
   for (int i = 0; i < DPL; ++i) acc[i] = 0.f;
   if (M != -kInf) {
     for (int s = 0; s < count; ++s) {
-      const size_t row = first + s * stride;
+      const size_t row = first + s;
       const float lv = ls[row];
       const float w = lv == -kInf ? 0.f : expf(lv - M);
       L += w;
