@@ -22,12 +22,10 @@
 //             32 keys; K stays in registers and V in LDS while 32-row Q / dO
 //             tiles stream through LDS: S = Q K^T and dP = dO V^T, then
 //             dV^T += dO^T P and dK^T += Q^T dS with P, dS straight from
-//             registers. For groups of an even size a work-group takes two
-//             query heads (eight waves, V shared) and sums their dK, dV in
-//             LDS. Each work-group writes its dK, dV: bf16 when it covers the
-//             whole group, fp32 partials otherwise.
-//   bwd_gsum  sums the fp32 partials over each K/V head's group (GQA) and
-//             rounds to bf16.
+//             registers. Each query head writes its own dK, dV (bf16 when the
+//             K/V head has one query head, fp32 partials otherwise).
+//   bwd_gsum  sums the fp32 partials over the G query heads of each K/V head
+//             (GQA) and rounds to bf16.
 // Splitting dK/dV work by query head keeps the causal work per work-group
 // balanced enough (heaviest key tiles first) with no cross-work-group
 // reduction other than the small group sum.
@@ -129,14 +127,13 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dk_part;  // [B, H, Nk, d] when G > 1 ([B, H / 2, Nk, d] with paired heads)
+  float* dk_part;  // [B, H, Nk, d] when G > 1
   float* dv_part;
   int B, H, Hkv, Nq, Nk, G;
   float scale, scale_log2;
   int causal, window;
   int nqt, nkt;
   int xcd_remap;
-  int pair;  // dK / dV work-groups take two query heads of a group (G even)
   // Packed documents (null for fixed-length calls): B documents whose query
   // and key rows are [cu_q[b], cu_q[b+1]) and [cu_k[b], cu_k[b+1]) of packed
   // sequences of Nq and Nk rows.
@@ -432,57 +429,45 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // dK, dV.
 
-//
-// PAIR: eight waves take two query heads h, h + 1 of one group for the same
-// 128 keys, four waves each (group grp = wave / 4), sharing the V tile; at
-// the end the two heads' dK, dV are summed through LDS, so a group of G
-// query heads leaves G / 2 fp32 partials (none for G = 2, which writes bf16).
-template <int D, bool PAIR>
-__global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void bwd_dkdv_kernel(
-    BwdParams p) {
+template <int D>
+__global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   using QT = LTile<D, 32>;   // one 32-row Q (or dO) step
   using VT = LTile<D, 128>;  // the work-group's V tile
   constexpr int KS = D / 16, DB = D / 32;
-  constexpr int NG = PAIR ? 2 : 1;  // query heads per work-group
-  // LDS: V tile, then per head the Q ring (2 steps) and the dO ring (2 steps).
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[VT::BYTES + NG * 4 * QT::BYTES];
-  // [head][slot][lse2, D][row]: rows 32..63 of each line take the zeros of
-  // the unused half of a 64-lane copy.
-  __shared__ __attribute__((aligned(256))) float stat[NG][2][2][64];
+  // LDS: V tile, then the Q ring (2 steps) and the dO ring (2 steps).
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[VT::BYTES + 4 * QT::BYTES];
+  // [slot][lse2, D][row]: rows 32..63 of each line take the zeros of the
+  // unused half of a 64-lane copy.
+  __shared__ __attribute__((aligned(256))) float stat[2][2][64];
   lds_u8* const L = lds_ptr(smem);
+  constexpr int VOFF = 0, QRING = VT::BYTES, DRING = VT::BYTES + 2 * QT::BYTES;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave_all = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int grp = PAIR ? wave_all >> 2 : 0;  // which query head of the work-group
-  const int wave = wave_all & 3;             // role within the head's four waves
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, g = lane >> 5;
-  constexpr int VOFF = 0;
-  const int QRING = VT::BYTES + grp * 4 * QT::BYTES, DRING = QRING + 2 * QT::BYTES;
 
   // Work-group -> (b, h, key tile): lowest key tiles (most visible query
-  // rows under a causal mask) first; with (B * units) % 8 == 0 the
-  // work-groups of one query head (or pair) share one XCD (their Q / dO
-  // streams overlap).
+  // rows under a causal mask) first; with (B * H) % 8 == 0 the work-groups
+  // of one query head share one XCD (their Q / dO streams overlap).
   int b, h, kt;
   {
     const int id = blockIdx.x;
-    const int nu = PAIR ? p.H / 2 : p.H;  // units per batch entry
-    const int bh = p.B * nu;
-    int u;
+    const int bh = p.B * p.H;
     if (p.xcd_remap) {
       const int xcd = id & 7, slot = id >> 3;
       const int per_rank = bh >> 3;
       const int rank = slot / per_rank, ul = slot - rank * per_rank;
-      u = ul * 8 + xcd;
+      const int u = ul * 8 + xcd;
+      b = u / p.H;
+      h = u - b * p.H;
       kt = rank;
     } else {
-      const int rank = id / bh;
-      u = id - rank * bh;
+      const int rank = id / bh, rem = id - rank * bh;
+      b = rem / p.H;
+      h = rem - b * p.H;
       kt = rank;
     }
-    b = u / nu;
-    h = PAIR ? 2 * (u - b * nu) + grp : u - b * nu;
   }
   const int kvh = h / p.G;
   const Rows R = rows_of(p, b, h, kvh);
@@ -564,7 +549,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
     if (wave < 2) {
       const uint32_t sbytes = r0 < Nq ? (uint32_t)(min((long long)Nq - r0, 32LL) * 4) : 0u;
       const float* src = (wave == 0 ? p.lse2 : p.delta) + head_q + rr;
-      dma4_async(rsrc_words(src, sbytes), lds_ptr(&stat[grp][slot][wave][0]), (uint32_t)lane * 4u);
+      dma4_async(rsrc_words(src, sbytes), lds_ptr(&stat[slot][wave][0]), (uint32_t)lane * 4u);
     }
   };
   // Does step st (rows [32 st, 32 st + 32)) need the per-element mask?
@@ -587,7 +572,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
   }
 
   if (nsteps > 0) {
-    if (grp == 0) {  // the V tile, shared by both heads of a pair
+    {
       const uint32_t vbytes = k0 < Nk ? (uint32_t)((Nk - k0) * VT::ROWB) : 0u;
       const i32x4 rv = rsrc_words(p.v + (head_kv + k0) * D, vbytes);
 #pragma unroll
@@ -679,8 +664,8 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
 #pragma unroll
       for (int c2 = 0; c2 < 2; ++c2) {
         const int c = hf * 2 + c2;  // rows 8 c + 4 g + (0..3)
-        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[grp][slot][0][8 * c + 4 * g]);
-        const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[grp][slot][1][8 * c + 4 * g]);
+        const f32x4 l2 = *reinterpret_cast<const f32x4*>(&stat[slot][0][8 * c + 4 * g]);
+        const f32x4 dl = *reinterpret_cast<const f32x4*>(&stat[slot][1][8 * c + 4 * g]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = c * 4 + e;
@@ -722,38 +707,9 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
   }
   mfma_drain();
 
-  if constexpr (PAIR) {
-    // dK, dV of the pair: the second head's waves hand their accumulators
-    // to the first head's waves with the same keys through LDS (free once
-    // every wave has left the loop), element e of thread t at float
-    // 256 e + t, so that each store and load of a wave is contiguous.
-    float* red = reinterpret_cast<float*>(smem);
-    const int t4 = tid & 255;
-    auto hand_over = [&](f32x16 (&acc)[DB]) {
-      __syncthreads();
-      if (grp == 1) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) red[(db * 16 + r) * 256 + t4] = acc[db][r];
-      }
-      __syncthreads();
-      if (grp == 0) {
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[db][r] += red[(db * 16 + r) * 256 + t4];
-      }
-    };
-    static_assert(DB * 16 * 256 * 4 <= VT::BYTES + NG * 4 * QT::BYTES, "hand-over fits the LDS");
-    hand_over(dka);
-    hand_over(dva);
-    if (grp == 1) return;
-  }
-
   // Lane (g, l32) holds key `key`, dims db*32 + 8 rr + 4 g + (0..3).
   if (kvalid) {
-    if (p.G == NG) {
+    if (p.G == 1) {
       uint16_t* kp = p.dk + (head_kv + key) * D + 4 * g;
       uint16_t* vp = p.dv + (head_kv + key) * D + 4 * g;
 #pragma unroll
@@ -769,13 +725,7 @@ __global__ __launch_bounds__(PAIR ? 2 * kThreads : kThreads, PAIR ? 1 : 2) void 
           *reinterpret_cast<uint2*>(vp + db * 32 + rr * 8) = wv;
         }
     } else {
-      // fp32 partial of this query head (or pair): row of head (or pair) u
-      // of this batch entry or, for packed documents, of the packed axis
-      const size_t head_p =
-          PAIR ? (p.cu_q == nullptr ? (size_t)(b * (p.H / 2) + h / 2) * p.Nk
-                                    : (size_t)(h / 2) * p.Nk + (R.head_kv - (size_t)kvh * p.Nk))
-               : R.head_p;
-      const size_t part = (head_p + key) * D + 4 * g;
+      const size_t part = (R.head_p + key) * D + 4 * g;
       float* kp = p.dk_part + part;
       float* vp = p.dv_part + part;
 #pragma unroll
@@ -802,10 +752,9 @@ __global__ __launch_bounds__(kThreads) void bwd_gsum_kernel(BwdParams p, int d, 
   const long long per_head = (long long)p.Nk * d / 8;
   const long long bkv = i / per_head, rem = i - bkv * per_head;
   const long long b = bkv / p.Hkv, kvh = bkv - b * p.Hkv;
-  const int np = p.pair ? p.G / 2 : p.G;  // partials per K/V head
   f32x8 sk = {}, sv = {};
-  for (int gh = 0; gh < np; ++gh) {
-    const size_t src = ((size_t)(b * p.Hkv * np + kvh * np + gh) * p.Nk * d) + (size_t)rem * 8;
+  for (int gh = 0; gh < p.G; ++gh) {
+    const size_t src = ((size_t)(b * p.H + kvh * p.G + gh) * p.Nk * d) + (size_t)rem * 8;
     const f32x4* kp = reinterpret_cast<const f32x4*>(p.dk_part + src);
     const f32x4* vp = reinterpret_cast<const f32x4*>(p.dv_part + src);
     const f32x4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
@@ -845,21 +794,13 @@ hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
                         0, stream);
     if (e != hipSuccess) return e;
   }
-  // Groups of an even number of query heads: two heads per dK / dV
-  // work-group (half the fp32 partials; none for groups of two).
-  prm.pair = prm.G % 2 == 0 ? 1 : 0;
-  const int units = prm.pair ? prm.H / 2 : prm.H;
-  const size_t nkv = (size_t)prm.B * units * prm.nkt;
+  const size_t nkv = (size_t)prm.B * prm.H * prm.nkt;
   if (nkv == 0) return hipSuccess;
-  // the dK / dV kernel groups work-groups by query head (or pair) per XCD
-  prm.xcd_remap = ((prm.B * units) % 8 == 0) ? 1 : 0;
-  if (prm.pair)
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, true>),
-                        dim3((unsigned)nkv), dim3(2 * kThreads), args, 0, stream);
-  else
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D, false>),
-                        dim3((unsigned)nkv), dim3(kThreads), args, 0, stream);
-  if (e != hipSuccess || prm.G <= 2) return e;
+  // the dK / dV kernel groups work-groups by query head per XCD
+  prm.xcd_remap = ((prm.B * prm.H) % 8 == 0) ? 1 : 0;
+  e = hipLaunchKernel(reinterpret_cast<const void*>(&bwd_dkdv_kernel<D>), dim3((unsigned)nkv),
+                      dim3(kThreads), args, 0, stream);
+  if (e != hipSuccess || prm.G == 1) return e;
   long long n8 = nb * prm.Hkv * prm.Nk * D / 8;
   int d = D;
   void* gargs[] = {&prm, &d, &n8};
@@ -909,7 +850,6 @@ hipError_t launch_bwd(const BwdArgs& a, hipStream_t stream) {
   p.nqt = ((a.cu_q != nullptr ? a.max_q : a.Nq) + 127) / 128;
   p.nkt = ((a.cu_q != nullptr ? a.max_k : a.Nk) + 127) / 128;
   p.xcd_remap = ((a.B * a.Hkv) % 8 == 0) ? 1 : 0;
-  p.pair = 0;
   if (log_enabled())
     fprintf(stderr, "[miattn] bwd d=%d dq_grid=%lld dkdv_grid=%lld G=%d\n", a.d,
             (long long)a.B * a.H * p.nqt, (long long)a.B * a.H * p.nkt, p.G);
