@@ -359,12 +359,13 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
       const long long base = (long long)kt * BN + 4 * g;
       const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
       const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
+      const KeyRange vis(rl, rh);
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-          s[kb][r] = ((c >= rl) & (c <= rh)) ? s[kb][r] : -kInf;
+          s[kb][r] = vis.holds(c) ? s[kb][r] : -kInf;
         }
     }
 
@@ -649,10 +650,11 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
       const long long base = (long long)st * 32 + 4 * g;  // row of register 0
       const int rl = (int)max(min(jq_lo - base, 33LL), -1LL);
       const int rh = (int)max(min(jq_hi - base, 33LL), -1LL);
+      const KeyRange vis(rl, rh);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = 8 * (r >> 2) + (r & 3);
-        s[r] = ((c >= rl) & (c <= rh)) ? s[r] : -kInf;
+        s[r] = vis.holds(c) ? s[r] : -kInf;
       }
     }
 

@@ -174,6 +174,23 @@ __device__ __forceinline__ bool wave_any(bool pred) {
   return __builtin_amdgcn_ballot_w64(pred) != 0;
 }
 
+// Boundary-tile masks test a compile-time key offset c >= 0 against a row's
+// clamped bounds, rl <= c <= rh. As one unsigned comparison:
+// c + neg_rl <= span with neg_rl = -rl and span = rh - rl, and for a row that
+// sees no key here (rh < rl) c + 1 <= 0, false for every c. The two values are
+// made opaque to the compiler, which would otherwise fold the clamped bounds
+// back into two 64-bit comparisons per score.
+struct KeyRange {
+  unsigned neg_rl, span;
+  __device__ __forceinline__ KeyRange(int rl, int rh) {
+    const bool none = rh < rl;
+    neg_rl = none ? 1u : (unsigned)(-rl);
+    span = none ? 0u : (unsigned)(rh - rl);
+    asm volatile("" : "+v"(neg_rl), "+v"(span));
+  }
+  __device__ __forceinline__ bool holds(int c) const { return (unsigned)c + neg_rl <= span; }
+};
+
 // Eight fp32 values to bf16, round to nearest even.
 __device__ __forceinline__ bf16x8 to_bf16x8(const f32x8 v) {
   return __builtin_convertvector(v, bf16x8);

@@ -391,19 +391,13 @@ void fwd_bf16_kernel(FwdParams p) {
     const long long base = (long long)kt * BN + 4 * g;
     const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
     const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
-    // rl <= c <= rh as one unsigned comparison, c - rl <= rh - rl; a row that
-    // sees no key here (rh < rl) gets c + 1 <= 0, false for every c. The two
-    // values are opaque to the compiler, which would otherwise fold the
-    // clamped bounds back into two 64-bit comparisons per score.
-    const bool none = rh < rl;
-    unsigned neg_rl = none ? 1u : (unsigned)(-rl), span = none ? 0u : (unsigned)(rh - rl);
-    asm volatile("" : "+v"(neg_rl), "+v"(span));
+    const KeyRange vis(rl, rh);
 #pragma unroll
     for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-        sacc[kb][r] = ((unsigned)c + neg_rl <= span) ? sacc[kb][r] : -kInf;
+        sacc[kb][r] = vis.holds(c) ? sacc[kb][r] : -kInf;
       }
   };
   auto row_max = [&](const f32x16 (&sacc)[T::KB]) -> float {
