@@ -319,7 +319,7 @@ def main():
     ap.add_argument("--cpu-seqs", type=int, default=64)
     ap.add_argument("--only", choices=["all", "prefill", "decode", "fp32", "packed", "kvlens", "window",
                                        "paged", "backward", "fp8", "packed_backward",
-                                       "prefill_d64"],
+                                       "prefill_d64", "kvlens_skewed"],
                     default="all", help="launch only one part (for profiling runs)")
     ap.add_argument("--sweep", action="store_true",
                     help="instead of the step: causal prefill over N = 1k..128k, one JSON line")
@@ -414,6 +414,9 @@ def main():
     ck = synth.inputs.DECODE_KVLENS
     kv_lens = synth.inputs.kv_lengths(0, ck.B, ck.Nk)
     kv_lens_dev = torch.from_numpy(kv_lens).to(dev)
+    # A skewed batch over the same cache: every eighth sequence full, the rest 512 keys.
+    sk_lens = synth.inputs.skewed_kv_lengths(ck.B, ck.Nk)
+    sk_lens_dev = torch.from_numpy(sk_lens).to(dev)
     # The same lengths stored in 16-key pages scattered over one pool.
     cg = synth.inputs.PAGED["decode"]
     page_size = synth.inputs.PAGED["page_size"]
@@ -452,6 +455,9 @@ def main():
         "kvlens": lambda: mi.attn_decode_varlen(qd, kc, vc, kv_lens_dev, scale=ck.scale,
                                                 window=ck.window, num_splits=ck.splits,
                                                 out=od, lse=lsed, workspace=ws),
+        "kvlens_skewed": lambda: mi.attn_decode_varlen(qd, kc, vc, sk_lens_dev, scale=ck.scale,
+                                                       window=ck.window, num_splits=ck.splits,
+                                                       out=od, lse=lsed, workspace=ws),
         "packed_backward": lambda: mi.attn_bwd_varlen(
             qp, kp, vp, op, lsep, dout_p, cu_dev, cu_dev, max(pk_lens), max(pk_lens),
             scale=cpk.scale, causal=cpk.causal, window=cpk.window, dq=dqp, dk=dkp, dv=dvp,
@@ -472,7 +478,8 @@ def main():
     }
     core = ["prefill", "decode", "fp32"]
     ext = [] if args.no_extensions else ["prefill_d64", "window", "fp8", "packed",
-                                         "packed_backward", "kvlens", "paged", "backward"]
+                                         "packed_backward", "kvlens", "kvlens_skewed", "paged",
+                                         "backward"]
     if args.only != "all":
         core, ext = [args.only], []
 
@@ -528,6 +535,7 @@ def main():
     dec_gbs = rate(dec_bytes, mean(dec_ms)) / 1e9
     pk_flops = accounting.packed_flops(cpk.H, pk_cu, pk_cu, cpk.d, cpk.causal, cpk.window)
     kvl_bytes = accounting.decode_kvlens_bytes(ck.H, ck.Hkv, kv_lens, ck.d, window=ck.window)
+    sk_bytes = accounting.decode_kvlens_bytes(ck.H, ck.Hkv, sk_lens, ck.d, window=ck.window)
     pg_bytes = accounting.decode_paged_bytes(cg.H, cg.Hkv, kv_lens, cg.d, page_size,
                                              window=cg.window)
     bwd_flops = accounting.backward_flops(cp.B, cp.H, cp.Nq, cp.Nk, cp.d, cp.causal, cp.window)
@@ -539,6 +547,7 @@ def main():
                      "fp32": (rate(f32_flops, mean(f32_ms)) / 1e12, "TFLOP/s"),
                      "packed": (rate(pk_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "kvlens": (rate(kvl_bytes, mean(xs)) / 1e9, "GB/s"),
+                     "kvlens_skewed": (rate(sk_bytes, mean(xs)) / 1e9, "GB/s"),
                      "paged": (rate(pg_bytes, mean(xs)) / 1e9, "GB/s"),
                      "backward": (rate(bwd_flops, mean(xs)) / 1e12, "TFLOP/s"),
                      "fp8": (rate(pre_flops, mean(xs)) / 1e12, "TFLOP/s"),
@@ -630,6 +639,16 @@ def main():
             "algorithmic_bytes": kvl_bytes,
             "ms": round(mean(ms["kvlens"]), 4), "ms_min": round(min(ms["kvlens"]), 4),
             "value": round(kv_gbs, 1), "unit": "GB/s", "frac_hbm": round(kv_gbs / PEAK_HBM_GBS, 4)}
+    if "kvlens_skewed" in ms:
+        sk_gbs = rate(sk_bytes, mean(ms["kvlens_skewed"])) / 1e9
+        out["decode_kvlens_skewed"] = {
+            "workload": f"split-K decode B{ck.B} H{ck.H} Hkv{ck.Hkv} d{ck.d} over the same cache "
+                        f"slots, every eighth sequence at {ck.Nk} keys and the rest at 512 "
+                        f"(total {int(sk_lens.sum())} keys), {ck.splits} splits",
+            "algorithmic_bytes": sk_bytes,
+            "ms": round(mean(ms["kvlens_skewed"]), 4),
+            "ms_min": round(min(ms["kvlens_skewed"]), 4),
+            "value": round(sk_gbs, 1), "unit": "GB/s", "frac_hbm": round(sk_gbs / PEAK_HBM_GBS, 4)}
     if "paged" in ms:
         pg_gbs = rate(pg_bytes, mean(ms["paged"])) / 1e9
         out["decode_paged"] = {

@@ -197,6 +197,14 @@ def kv_lengths(seed: int, B: int, Nk: int, lo: int = 1) -> np.ndarray:
     return rng.integers(lo, Nk + 1, size=B).astype(np.int32)
 
 
+def skewed_kv_lengths(B: int, Nk: int, every: int = 8, short: int = 512) -> np.ndarray:
+    """int32 [B]: a serving batch dominated by a few long contexts: every
+    `every`-th sequence holds all Nk keys, the others `short` keys."""
+    lens = np.full(B, min(short, Nk), dtype=np.int32)
+    lens[::every] = Nk
+    return lens
+
+
 @dataclass(frozen=True)
 class PackedConfig:
     name: str

@@ -11,8 +11,8 @@ max-abs and mean-abs bounds taken over the whole tensor:
 * split-K decode, B64 H32 Hkv8 Nk32768 d128, 16 splits: every sequence and
   head, one sequence of the cache at a time on the host;
 * packed documents (four 8k contexts, H32 Hkv8): every row of every head;
-* decode with per-sequence lengths, and the same over 16-key pages: every
-  sequence and head.
+* decode with per-sequence lengths, the same over 16-key pages, and a skewed
+  batch (every eighth sequence full, the rest 512 keys): every sequence and head.
 
 The causal sliding-window prefill over 32768 tokens (window 4096) would need
 the full 32768 x 32768 score matrix per head in the oracle, so it is compared
@@ -171,6 +171,29 @@ def test_decode_kvlens_every_output(seed):
                                              0, heads)
 
     decode_all_sequences(o, lse, ref, c.B, f"{c.name} seed {seed}")
+    del kc, vc
+    torch.cuda.empty_cache()
+
+
+def test_decode_skewed_lengths_every_output():
+    """The bench's skewed batch: every eighth sequence holds all 32768 keys, the rest 512;
+    balanced pieces spread each long sequence over many work-groups."""
+    c = S.DECODE_KVLENS
+    lens = S.skewed_kv_lengths(c.B, c.Nk)
+    note(f"skewed decode: {int(lens.sum())} keys, GPU")
+    q, kc, vc = S.decode_inputs(c, 0, device=DEV)
+    o, lse = mi.attn_decode_varlen(q, kc, vc, torch.from_numpy(lens).to(DEV), scale=c.scale,
+                                   num_splits=c.splits)
+    torch.cuda.synchronize()
+    heads = list(range(c.H))
+
+    def ref(b):
+        n = int(lens[b])
+        return oracle.decode_kvlens_rows_ref(q[b:b + 1].cpu(), kc[b:b + 1, :, :n].cpu(),
+                                             vc[b:b + 1, :, :n].cpu(), [n], c.scale, c.window,
+                                             0, heads)
+
+    decode_all_sequences(o, lse, ref, c.B, "skewed decode")
     del kc, vc
     torch.cuda.empty_cache()
 
