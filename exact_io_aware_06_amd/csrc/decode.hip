@@ -9,9 +9,11 @@
 // work-group that reads its K/V rows exactly once for all G query heads
 // sharing that KV head. With per-sequence lengths, a small plan kernel lays
 // the visible keys of all sequences end to end in tiles, and each of the
-// B * S work-groups per KV head takes an equal run of whole tiles, cut at
-// sequence boundaries into pieces (one partial each), so a long sequence in a
-// batch of short ones is spread over the machine instead of over S chunks.
+// work-groups per KV head (at most B * S, and at most one round of the
+// work-groups the device holds at once) takes an equal run of whole tiles,
+// cut at sequence boundaries into pieces (one partial each), so a long
+// sequence in a batch of short ones is spread over the machine instead of
+// over S chunks.
 //
 // A paged cache changes only where a key row is read from: row j of a
 // sequence lives in page block_table[b][j / page_size] of a page pool, at row
@@ -37,6 +39,7 @@
 // O = sum_s exp(lse_s - LSE) O_s; chunks with no visible key have
 // lse_s = -inf and weigh nothing.
 
+#include <algorithm>
 #include <cstdio>
 #include <mutex>
 
@@ -56,6 +59,11 @@ namespace {
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
+// Work-groups of the balanced split kernel (d = 128, d = 64) resident on a
+// device at once (compute units x work-groups per compute unit); 0 = not yet
+// queried.
+std::mutex g_slots_mu;
+int g_slots[kMaxDevices][2] = {};
 }  // namespace
 
 hipError_t decode_scratch(int device, void** ptr) {
@@ -116,7 +124,8 @@ struct MergeParams {
 struct PlanParams {
   const int* kv_lens;
   int* tcum;
-  int B, Nk, window, W;
+  int B, Nk, window;
+  int W;  // work-groups of the split grid per (KV head, head block)
 };
 
 template <int D>
@@ -339,7 +348,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
       {
         const uint16_t* kp = ks + (wave * 32 + l32) * T::KSTR + g * 8;
 #pragma unroll
-        for (int st = 0; st < T::KS; ++st) sacc = mfma32x32x16(lds_read_bf16x8(kp + st * 16), qf[st], sacc);
+        for (int st = 0; st < T::KS; ++st)
+          sacc = mfma32x32x16(lds_read_bf16x8(kp + st * 16), qf[st], sacc);
       }
       mfma_drain();
       if (t0 + kBN > hi) {
@@ -404,7 +414,8 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr)
           *reinterpret_cast<f32x4*>(dst + db * 32 + rr * 8) =
-              f32x4{oacc[db][rr * 4], oacc[db][rr * 4 + 1], oacc[db][rr * 4 + 2], oacc[db][rr * 4 + 3]};
+              f32x4{oacc[db][rr * 4], oacc[db][rr * 4 + 1], oacc[db][rr * 4 + 2],
+                    oacc[db][rr * 4 + 3]};
       if (g == 0) {
         mw[wave * 32 + l32] = m_ref;
         lbw[wave * 32 + l32] = lb_col;
@@ -529,7 +540,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
       const float w = lv == -kInf ? 0.f : expf(lv - M);
       L += w;
 #pragma unroll
-      for (int i = 0; i < DPL; ++i) acc[i] = __builtin_fmaf(w, os[row * D + lane * DPL + i], acc[i]);
+      for (int i = 0; i < DPL; ++i)
+        acc[i] = __builtin_fmaf(w, os[row * D + lane * DPL + i], acc[i]);
     }
   }
   const float inv = L > 0.f ? 1.f / L : 0.f;
@@ -548,6 +560,27 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(MergeParams p) {
 // Partial rows: B * H * S for equal chunks; with balanced pieces, one per
 // (work-group share w < B * S, sequence b) pair that can occur, indexed
 // w + b < B * (S + 1), per query head. Then the plan: B + 2 + B * S ints.
+// Resident work-groups of split-kernel instantiation `which` (launched with
+// kThreads threads) on the current device, cached per device.
+hipError_t resident_work_groups(int which, const void* fn, int* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_slots_mu);
+  int& v = g_slots[dev][which];
+  if (v == 0) {
+    int cus = 0, per_cu = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, kThreads, 0);
+    if (e != hipSuccess) return e;
+    v = max(1, cus * per_cu);
+  }
+  *out = v;
+  return hipSuccess;
+}
+
 size_t decode_workspace_bytes(int B, int H, int d, int splits) {
   const size_t rows = (size_t)B * H * (splits + 1);
   return rows * (size_t)(d + 1) * sizeof(float) + ((size_t)B * (splits + 1) + 2) * sizeof(int);
@@ -583,23 +616,6 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   sp.scale = a.scale;
   sp.scale_log2 = a.scale * kLog2e;
   sp.thr_raw = kRescaleThreshold / sp.scale_log2;
-  // Both layouts launch B * S work-groups per (KV head, head block).
-  const unsigned nsplit_blk = (unsigned)((size_t)a.B * a.Hkv * sp.HB * a.splits);
-  if (log_enabled())
-    fprintf(stderr,
-            "[miattn] decode d=%d splits=%d kv_lens=%s page_size=%d split_grid=%u "
-            "merge_grid=%d\n",
-            a.d, a.splits, bal ? "per-sequence (balanced pieces)" : "uniform",
-            a.block_table != nullptr ? a.page_size : 0, nsplit_blk, a.B * a.H);
-  hipError_t e;
-  if (bal) {
-    PlanParams pp{a.kv_lens, plan, a.B, a.Nk, a.window, a.B * a.splits};
-    void* pargs[] = {&pp};
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_plan_kernel), dim3(1),
-                        dim3(kThreads), pargs, 0, stream);
-    if (e != hipSuccess) return e;
-  }
-  void* sargs[] = {&sp};
   const bool paged = a.block_table != nullptr;
   const void* sfn;
   if (a.d == 128)
@@ -610,6 +626,40 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     sfn = paged ? reinterpret_cast<const void*>(&decode_split_kernel<64, true, true>)
           : bal ? reinterpret_cast<const void*>(&decode_split_kernel<64, false, true>)
                 : reinterpret_cast<const void*>(&decode_split_kernel<64, false, false>);
+  // Equal chunks: B * S work-groups per (KV head, head block). Balanced
+  // pieces: at most B * S, and no more than one round of the work-groups the
+  // device holds at once, so each takes one long equal run of tiles (fewer,
+  // longer work-groups pay the plan reads and the combine less often, and no
+  // work-group waits for a second round).
+  const size_t units = (size_t)a.Hkv * sp.HB;
+  size_t per_unit = (size_t)a.B * a.splits;
+  hipError_t e;
+  if (bal) {
+    // Sized from the contiguous instantiation for both caches, so that a paged
+    // cache and a contiguous one holding the same keys get the same pieces.
+    const void* sized = a.d == 128
+                            ? reinterpret_cast<const void*>(&decode_split_kernel<128, false, true>)
+                            : reinterpret_cast<const void*>(&decode_split_kernel<64, false, true>);
+    int slots = 0;
+    e = resident_work_groups(a.d == 128 ? 0 : 1, sized, &slots);
+    if (e != hipSuccess) return e;
+    per_unit = std::min(per_unit, std::max<size_t>(1, (size_t)slots / units));
+  }
+  const unsigned nsplit_blk = (unsigned)(units * per_unit);
+  if (log_enabled())
+    fprintf(stderr,
+            "[miattn] decode d=%d splits=%d kv_lens=%s page_size=%d split_grid=%u "
+            "merge_grid=%d\n",
+            a.d, a.splits, bal ? "per-sequence (balanced pieces)" : "uniform",
+            a.block_table != nullptr ? a.page_size : 0, nsplit_blk, a.B * a.H);
+  if (bal) {
+    PlanParams pp{a.kv_lens, plan, a.B, a.Nk, a.window, (int)per_unit};
+    void* pargs[] = {&pp};
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_plan_kernel), dim3(1),
+                        dim3(kThreads), pargs, 0, stream);
+    if (e != hipSuccess) return e;
+  }
+  void* sargs[] = {&sp};
   e = hipLaunchKernel(sfn, dim3(nsplit_blk), dim3(kThreads), sargs, 0, stream);
   if (e != hipSuccess) return e;
 

@@ -270,8 +270,10 @@ int attn_decode_splitk_noalloc(const void* q, const void* k_cache, const void* v
  * its query sits at position kv_lens[b] - 1. The work follows the real
  * lengths and is balanced over the batch: the visible keys of all sequences
  * are laid end to end in tiles of 128 (each sequence's run starting at its
- * first visible key), and each of the B * num_splits work-groups per KV head
- * takes an equal run of whole tiles, cut at sequence boundaries into pieces
+ * first visible key), and each of the work-groups per KV head (B *
+ * num_splits of them at most, and no more than fit on the device at once,
+ * so that each takes one long run) takes an equal run of whole tiles, cut at
+ * sequence boundaries into pieces
  * that each yield one partial (O_s, lse_s) of one sequence; the merge then
  * combines a sequence's pieces as above. A small first kernel builds this
  * plan from kv_lens on the device, so the call needs no host copy of the

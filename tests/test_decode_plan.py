@@ -2,8 +2,9 @@
 
 With per-sequence cache lengths the decode does not cut each sequence into S
 equal chunks. It lays the visible keys of all sequences end to end in tiles of
-128 keys and hands each of the B * S work-groups per KV head an equal run of
-whole tiles; a run that crosses a sequence boundary yields one partial result
+128 keys and hands each of its W work-groups per KV head (at most B * S; the
+launch caps W at one round of the work-groups the device holds at once) an
+equal run of whole tiles; a run that crosses a sequence boundary yields one partial result
 per sequence it touches, and the partial of (work-group w, sequence b) is
 stored as partial w + b. The merge finds a sequence's partials from the
 running tile counts alone.
@@ -53,9 +54,12 @@ def plan(lens, Nk, window, W):
     return T, budget, first
 
 
-def run_plan(lens, Nk, window, S):
+def run_plan(lens, Nk, window, S, W=None):
+    """W: work-groups per KV head, at most B * S (the launch caps it at one round of the
+    device's resident work-groups)."""
     B = len(lens)
-    W = B * S
+    W = B * S if W is None else W
+    assert 1 <= W <= B * S
     T, budget, first = plan(lens, Nk, window, W)
     total = T[B]
     written = {}
@@ -106,6 +110,7 @@ def test_plan_covers_keys_once_with_unique_partials(seed):
         window = rng.choice([0, 0, 1, 40, 200, 4096])
         lens = [rng.choice([0, 1, Nk, rng.randint(0, Nk)]) for _ in range(B)]
         run_plan(lens, Nk, window, S)
+        run_plan(lens, Nk, window, S, W=rng.randint(1, B * S))
 
 
 def test_plan_equal_full_lengths_are_the_equal_chunks():

@@ -259,9 +259,9 @@ def test_decode_varlen_large_batch():
 
 
 def test_decode_varlen_skewed_batch():
-    """One long sequence among one-key ones (157 + 31 tiles for 512 work-groups per KV head):
-    each work-group takes one tile, so the long sequence's keys come back as 157 partials,
-    which the merge combines over three rounds of its 64 lanes."""
+    """One long sequence among one-key ones (157 + 31 tiles for up to 512 work-groups per KV
+    head): each work-group takes one tile, so the long sequence's keys come back as 157
+    partials, which the merge combines over three rounds of its 64 lanes."""
     lens = [20000] + [1] * 31
     q, kc, vc = decode_case(len(lens), 8, 2, 20000, 128, seed=12)
     o, lse = run_decode(q, kc, vc, lens, 0.088, 0, 16)
