@@ -64,12 +64,14 @@ def run_all(x):
     od, ld = mi.attn_decode(x["qd"], x["kc"], x["vc"], scale=s, num_splits=7)
     og, lg = mi.attn_decode_paged(x["qd"], x["kpg"], x["vpg"], x["table"], x["lens"], scale=s,
                                   num_splits=5)
+    # the same keys in the contiguous cache with per-sequence lengths (plan, pieces, merge)
+    ov, lv = mi.attn_decode_varlen(x["qd"], x["kc"], x["vc"], x["lens"], scale=s, num_splits=5)
     # the no-allocation decode (its partials in the library's own scratch)
     on = torch.empty_like(x["qd"])
     ln = torch.empty(x["qd"].shape[:2], dtype=torch.float32, device=DEV)
     mi.attn_decode_splitk_noalloc(x["qd"], x["kc"], x["vc"], on, ln, scale=s, num_splits=7)
     return {"o": o, "lse": lse, "dq": dq, "dk": dk, "dv": dv, "op": op, "lp": lp, "od": od,
-            "ld": ld, "og": og, "lg": lg, "on": on, "ln": ln}
+            "ld": ld, "og": og, "lg": lg, "ov": ov, "lv": lv, "on": on, "ln": ln}
 
 
 def test_graph_replays_match_eager():
@@ -105,5 +107,7 @@ def test_graph_replays_match_eager():
         torch.cuda.synchronize()
         for name, ref in eager.items():
             assert torch.equal(outs[name], ref), f"replay {rep}: {name} differs from the eager call"
-    # the no-allocation decode equals the decode with a workspace
+    # the no-allocation decode equals the decode with a workspace, and the paged cache the
+    # contiguous one holding the same keys
     assert torch.equal(eager["on"], eager["od"]) and torch.equal(eager["ln"], eager["ld"])
+    assert torch.equal(eager["og"], eager["ov"]) and torch.equal(eager["lg"], eager["lv"])
