@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
   //    C = ceil(n / S), or
   //  * balanced pieces (BAL): the work-group's share [g_lo, g_hi) of the
   //    batch's visible key tiles laid end to end (sequence b owns tiles
-  //    [Tc[b], Tc[b + 1]) of that list, starting at its first visible key),
+  //    [tcum[b], tcum[b + 1]) of that list, starting at its first visible key),
   //    cut at sequence boundaries into pieces; the piece of (work-group w,
   //    sequence b) is partial w + b among each query head's B (S + 1) rows.
   // Grid order: split (work-group share) slowest. Consecutive work-groups are
