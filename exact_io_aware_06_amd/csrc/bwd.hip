@@ -748,18 +748,25 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // GQA: dK, dV of a K/V head = sum over its G query heads' partials.
 
+// One thread per 8 consecutive elements of a K/V head's dK and dV. The
+// partials are read once, so they are loaded non-temporally; with G known at
+// compile time every head's loads are issued before the first add. The sum
+// runs over gh = 0 .. G-1 in that order either way.
+template <int GC>
 __global__ __launch_bounds__(kThreads) void bwd_gsum_kernel(BwdParams p, int d, long long n8) {
   const long long i = (long long)blockIdx.x * kThreads + threadIdx.x;  // 8-element group
   if (i >= n8) return;
+  const int G = GC > 0 ? GC : p.G;
   const long long per_head = (long long)p.Nk * d / 8;
   const long long bkv = i / per_head, rem = i - bkv * per_head;
   const long long b = bkv / p.Hkv, kvh = bkv - b * p.Hkv;
+  const size_t head_stride = (size_t)p.Nk * d;
+  const size_t src0 = ((size_t)(b * p.H + kvh * G) * p.Nk * d) + (size_t)rem * 8;
+  const f32x4* kp = reinterpret_cast<const f32x4*>(p.dk_part + src0);
+  const f32x4* vp = reinterpret_cast<const f32x4*>(p.dv_part + src0);
+  const size_t hs4 = head_stride / 4;
   f32x8 sk = {}, sv = {};
-  for (int gh = 0; gh < p.G; ++gh) {
-    const size_t src = ((size_t)(b * p.H + kvh * p.G + gh) * p.Nk * d) + (size_t)rem * 8;
-    const f32x4* kp = reinterpret_cast<const f32x4*>(p.dk_part + src);
-    const f32x4* vp = reinterpret_cast<const f32x4*>(p.dv_part + src);
-    const f32x4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
+  auto add = [&](f32x4 k0, f32x4 k1, f32x4 v0, f32x4 v1) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       sk[e] += k0[e];
@@ -767,6 +774,22 @@ __global__ __launch_bounds__(kThreads) void bwd_gsum_kernel(BwdParams p, int d, 
       sv[e] += v0[e];
       sv[e + 4] += v1[e];
     }
+  };
+  if constexpr (GC > 0) {
+    f32x4 k0[GC], k1[GC], v0[GC], v1[GC];
+#pragma unroll
+    for (int gh = 0; gh < GC; ++gh) {
+      k0[gh] = __builtin_nontemporal_load(kp + gh * hs4);
+      k1[gh] = __builtin_nontemporal_load(kp + gh * hs4 + 1);
+      v0[gh] = __builtin_nontemporal_load(vp + gh * hs4);
+      v1[gh] = __builtin_nontemporal_load(vp + gh * hs4 + 1);
+    }
+#pragma unroll
+    for (int gh = 0; gh < GC; ++gh) add(k0[gh], k1[gh], v0[gh], v1[gh]);
+  } else {
+    for (int gh = 0; gh < G; ++gh)
+      add(__builtin_nontemporal_load(kp + gh * hs4), __builtin_nontemporal_load(kp + gh * hs4 + 1),
+          __builtin_nontemporal_load(vp + gh * hs4), __builtin_nontemporal_load(vp + gh * hs4 + 1));
   }
   const size_t dst = (size_t)i * 8;
   uint4 wk, wv;
@@ -806,7 +829,11 @@ hipError_t launch_bwd_d(BwdParams& prm, hipStream_t stream) {
   long long n8 = nb * prm.Hkv * prm.Nk * D / 8;
   int d = D;
   void* gargs[] = {&prm, &d, &n8};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&bwd_gsum_kernel),
+  const void* gfn = prm.G == 2   ? reinterpret_cast<const void*>(&bwd_gsum_kernel<2>)
+                    : prm.G == 4 ? reinterpret_cast<const void*>(&bwd_gsum_kernel<4>)
+                    : prm.G == 8 ? reinterpret_cast<const void*>(&bwd_gsum_kernel<8>)
+                                 : reinterpret_cast<const void*>(&bwd_gsum_kernel<0>);
+  return hipLaunchKernel(gfn,
                          dim3((unsigned)((n8 + kThreads - 1) / kThreads)), dim3(kThreads), gargs,
                          0, stream);
 }
