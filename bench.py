@@ -163,7 +163,7 @@ def write_traffic(fetch_csv: str, write_csv: str, skip: int, copy_mib: int) -> d
     cp = synth.CONFIGS["causal_gqa_n8192_d128"]
     cd = synth.CONFIGS["decode_b64_nk32768_d128"]
     want = {
-        "fwd_bf16": (("fwd_bf16_kernel<128, false, false>", cp.B * cp.H * (cp.Nq // 128)),
+        "fwd_bf16": (("fwd_bf16_kernel<128, false, false, true>", cp.B * cp.H * (cp.Nq // 128)),
                      accounting.prefill_bytes(cp.B, cp.H, cp.Hkv, cp.Nq, cp.Nk, cp.d)),
         "decode": (("decode_split_kernel<128, false, false>", cd.B * cd.Hkv * cd.splits),
                    accounting.decode_bytes(cd.B, cd.H, cd.Hkv, cd.Nk, cd.d)),

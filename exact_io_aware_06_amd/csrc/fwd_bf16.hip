@@ -173,7 +173,8 @@ __device__ __forceinline__ void decode_workgroup(const FwdParams& p, int id, int
   }
 }
 
-template <int D, bool COUNT, bool FP8 = false>
+// CAUSAL0: causal with no window, where only the diagonal bound can mask a key.
+template <int D, bool COUNT, bool FP8 = false, bool CAUSAL0 = false>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 && !FP8 ? 3 : 2)))
 void fwd_bf16_kernel(FwdParams p) {
   using T = Tile<D, FP8>;
@@ -236,6 +237,11 @@ void fwd_bf16_kernel(FwdParams p) {
   const long long lo_q = p.window > 0 ? qpos - p.window : 0;
   long long hi_q = p.causal ? qpos : (p.window > 0 ? qpos + p.window : (long long)Nk - 1);
   hi_q = min(hi_q, (long long)Nk - 1);
+  // The same bounds in 32 bits, clamped to [-2 BN, Nk + 2 BN]: a visited key
+  // tile starts in [0, Nk), so every bound relative to it clamps to the same
+  // value in [-1, BN + 1] as the unclamped one.
+  const int lo_c = (int)max(min(lo_q, (long long)Nk + 2 * BN), -2LL * BN);
+  const int hi_c = (int)max(min(hi_q, (long long)Nk + 2 * BN), -2LL * BN);
   bf16x8 qf[FP8 ? 1 : T::KS];
   i32x8 qf8[FP8 ? T::KS8 : 1];
   if constexpr (FP8) {
@@ -387,18 +393,30 @@ void fwd_bf16_kernel(FwdParams p) {
   // the candidate reference max and whether it must replace m_ref.
   auto mask_tile = [&](int kt, f32x16 (&sacc)[T::KB]) {
     // Key kt*BN + c + 4g is visible iff lo_q <= key <= hi_q; compare the
-    // compile-time offset c against the row's bounds relative to the tile.
-    const long long base = (long long)kt * BN + 4 * g;
-    const int rl = (int)max(min(lo_q - base, (long long)BN + 1), -1LL);
-    const int rh = (int)max(min(hi_q - base, (long long)BN + 1), -1LL);
-    const KeyRange vis(rl, rh);
+    // compile-time offset c against the row's bounds relative to the tile,
+    // clamped to [-1, BN + 1].
+    const int base = kt * BN + 4 * g;
+    int rl = min(max(lo_c - base, -1), BN + 1);
+    int rh = min(max(hi_c - base, -1), BN + 1);
+    asm volatile("" : "+v"(rl), "+v"(rh));  // keep the comparisons in 32 bits
+    auto apply = [&](auto vis) {
 #pragma unroll
-    for (int kb = 0; kb < T::KB; ++kb)
+      for (int kb = 0; kb < T::KB; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
-        sacc[kb][r] = vis.holds(c) ? sacc[kb][r] : -kInf;
-      }
+        for (int r = 0; r < 16; ++r) {
+          const int c = kb * 32 + 8 * (r >> 2) + (r & 3);
+          sacc[kb][r] = vis(c) ? sacc[kb][r] : -kInf;
+        }
+    };
+    if constexpr (CAUSAL0) {
+      // Causal without a window: every row sees keys from 0, so rl <= 0 <= c
+      // and one comparison per score against the diagonal bound decides (a
+      // row with no key in this tile has rh = -1).
+      apply([&](int c) { return c <= rh; });
+    } else {
+      const KeyRange vis(rl, rh);
+      apply([&](int c) { return vis.holds(c); });
+    }
   };
   auto row_max = [&](const f32x16 (&sacc)[T::KB]) -> float {
     float mx = -kInf;
@@ -676,8 +694,11 @@ template <int D>
 hipError_t launch_d(const FwdParams& prm, hipStream_t stream, bool count, bool fp8) {
   const unsigned nblk = (unsigned)((size_t)prm.B * prm.H * prm.nqt);
   void* args[] = {const_cast<FwdParams*>(&prm)};
-  const void* fn = fp8     ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false, true>)
+  const bool c0 = prm.causal && prm.window == 0;
+  const void* fn = fp8 ? (c0 ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false, true, true>)
+                             : reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false, true>))
                    : count ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, true>)
+                   : c0    ? reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false, false, true>)
                            : reinterpret_cast<const void*>(&fwd_bf16_kernel<D, false>);
   return hipLaunchKernel(fn, dim3(nblk), dim3(kThreads), args, 0, stream);
 }
