@@ -669,8 +669,13 @@ void fwd_bf16_kernel(FwdParams p) {
   const float lb = l_b + swap_halves(l_b);
   const float lf = l_f + swap_halves(l_f);
   const float inv = lb > 0.f ? 1.f / lb : 0.f;
-  if (qvalid) {
-    uint16_t* op = p.o + (head_q + qrow) * D + 4 * g;
+  // This lane's row, recomputed from the lane counter rather than kept live
+  // across the key loop (the loop has no register to spare for it).
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int ge = lane_e >> 5;
+  const int qrow_e = q0 + wave * 32 + (lane_e & 31);
+  if (qrow_e < Nq) {
+    uint16_t* op = p.o + (head_q + qrow_e) * D + 4 * ge;
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
@@ -680,8 +685,8 @@ void fwd_bf16_kernel(FwdParams p) {
         w.y = pack_bf16x2(oacc[db][rr * 4 + 2] * inv, oacc[db][rr * 4 + 3] * inv);
         *reinterpret_cast<uint2*>(op + db * 32 + rr * 8) = w;
       }
-    if (g == 0 && p.lse != nullptr)
-      p.lse[head_q + qrow] = lf > 0.f ? m_ref * p.scale + fast_log2(lf) * kLn2 : -kInf;
+    if (ge == 0 && p.lse != nullptr)
+      p.lse[head_q + qrow_e] = lf > 0.f ? m_ref * p.scale + fast_log2(lf) * kLn2 : -kInf;
   }
   if (COUNT && tid == 0) {
     int* c = p.counts + 2 * ((size_t)(b * p.H + h) * p.nqt + qt);
