@@ -86,6 +86,9 @@ def test_fwd_invalid_arguments(lib, f32):
     assert fwd(lib, scale=float("inf"), f32=f32) == EINVAL
     assert fwd(lib, d=96, f32=f32) == EUNSUP
     assert fwd(lib, d=256, f32=f32) == EUNSUP
+    # K / V of one head are addressed through 32-bit buffer offsets: Nk d 4 < 2^32
+    assert fwd(lib, Nk=0xFFFFFFFF // (128 * 4) + 1, d=128, f32=f32) == EUNSUP
+    assert fwd(lib, Nk=0xFFFFFFFF // (64 * 4) + 1, d=64, f32=f32) == EUNSUP
 
 
 @pytest.mark.parametrize("f32", [False, True])
@@ -296,6 +299,7 @@ def _no_gpu():
 def test_valid_call_without_device_reports_nodevice(lib):
     # All arguments valid, no HIP device in this process: ENODEVICE, no crash.
     assert fwd(lib) == ENODEV
+    assert fwd(lib, Nk=0xFFFFFFFF // (128 * 4), d=128) == ENODEV  # the longest key range
     assert dec(lib) == ENODEV
     assert vfwd(lib) == ENODEV
     assert vdec(lib) == ENODEV

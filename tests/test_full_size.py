@@ -266,3 +266,43 @@ def test_causal_context_sweep(N):
     compare(og, o_ref, lg, l_ref, f"{c.name} ({what})")
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+
+
+# The longest key range the C ABI takes for one head: the K / V rows of one
+# head are addressed through 32-bit buffer offsets, so Nk * d * 4 must stay
+# below 2^32 (8,388,607 keys at d = 128; one more is refused, tests/test_abi.py).
+NK_MAX_D128 = 0xFFFFFFFF // (128 * 4)
+MAX_ROWS = np.array([0, 1, 63, 64, 127, 128, 129, 190, 199])
+
+
+@pytest.mark.parametrize("causal,window", [(0, 0), (1, 5000)])
+def test_longest_key_range(causal, window):
+    """Two query heads of one K/V head against 8,388,607 keys (Nq = 200, so the
+    second query tile is ragged). Non-causal, every row sees every key; causal
+    with a window, the rows sit at the far end of the keys, so the tiles
+    visited are the last ones and their buffer offsets the largest. Sampled
+    rows of both heads (first and last rows of each query tile) against the
+    oracle, each row against all keys."""
+    c = synth.CONFIGS["window4096_gqa_n32768_d128"].with_(
+        name=f"max_keys_c{causal}_w{window}", B=1, H=2, Hkv=1, Nq=200, Nk=NK_MAX_D128,
+        causal=causal, window=window)
+    note(f"{c.name}: GPU, Nk = {c.Nk}")
+    q, k, v = synth.prefill_inputs(c, 0, device=DEV)
+    o, lse = mi.attn_fwd(q, k, v, scale=c.scale, causal=causal, window=window)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    qh = q.cpu()
+    # K / V widened once on the host (8.6 GB each), shared by both heads' rows
+    kh = k.cpu().to(torch.float64).numpy()
+    vh = v.cpu().to(torch.float64).numpy()
+    del k, v
+    torch.cuda.empty_cache()
+    o_ref = np.empty((c.H, MAX_ROWS.size, c.d))
+    l_ref = np.empty((c.H, MAX_ROWS.size))
+    for h in range(c.H):
+        o_ref[h], l_ref[h] = oracle.attention_rows_ref(qh, kh, vh, c.scale, causal, window, 0,
+                                                       h, MAX_ROWS)
+    note(f"{c.name}: oracle on {MAX_ROWS.size} rows x {c.H} heads {time.perf_counter() - t0:.1f} s")
+    compare(to64(o[0][:, MAX_ROWS]), o_ref, to64(lse[0][:, MAX_ROWS]), l_ref, c.name)
+    del q, o, lse, kh, vh
+    torch.cuda.empty_cache()
