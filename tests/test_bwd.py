@@ -187,3 +187,17 @@ def test_bwd_workload_causal_gqa_one_group():
     do = torch.randn(q.shape, generator=g).to(torch.bfloat16)
     worst, _ = check(q, k, v, do, c.scale, c.causal, c.window, kv_heads=[5], label="c3 group 5")
     assert worst <= 1.0
+
+
+def test_bwd_longest_key_range():
+    """The longest key range the C ABI takes for one head (8,388,607 keys at
+    d = 128: one head's K / V rows are addressed through 32-bit buffer
+    offsets), causal with a 5000-key window, two query heads of one K/V head
+    and 32 query rows at the far end: the keys that receive gradients are the
+    last ones, at the largest offsets, and every other key's dk / dv is
+    compared too (the oracle's are zero). Every output against the oracle."""
+    Nk = 0xFFFFFFFF // (128 * 4)
+    q, k, v, do = inputs(1, 2, 1, 32, Nk, 128, seed=21)
+    scale = float(np.float32(1 / math.sqrt(128)))
+    worst, _ = check(q, k, v, do, scale, 1, 5000, label="longest key range")
+    assert worst <= 1.0
