@@ -306,3 +306,26 @@ def test_longest_key_range(causal, window):
     compare(to64(o[0][:, MAX_ROWS]), o_ref, to64(lse[0][:, MAX_ROWS]), l_ref, c.name)
     del q, o, lse, kh, vh
     torch.cuda.empty_cache()
+
+
+def test_decode_cache_past_4_gib():
+    """Decode over caches larger than 4 GiB per tensor (three sequences of
+    6,000,007 keys, H8 Hkv1 d128: 4.6 GB each for K and V), so the third
+    sequence's rows sit at byte offsets beyond 2^32; the library's split
+    count. Every sequence and head against the oracle."""
+    c = synth.CONFIGS["decode_b64_nk32768_d128"].with_(name="decode_past_4gib", B=3, H=8, Hkv=1,
+                                                       Nk=6_000_007, splits=0)
+    assert c.Nk * c.d * 2 * (c.B - 1) < 2 ** 32 < c.Nk * c.d * 2 * c.B
+    note(f"{c.name}: GPU")
+    q, kc, vc = synth.decode_inputs(c, seed=0, device=DEV)
+    o, lse = mi.attn_decode(q, kc, vc, scale=c.scale, num_splits=0)
+    torch.cuda.synchronize()
+    heads = list(range(c.H))
+
+    def ref(b):
+        return oracle.decode_rows_ref(q[b:b + 1].cpu(), kc[b:b + 1].cpu(), vc[b:b + 1].cpu(),
+                                      c.scale, c.window, 0, heads)
+
+    decode_all_sequences(o, lse, ref, c.B, c.name)
+    del kc, vc
+    torch.cuda.empty_cache()
