@@ -175,7 +175,8 @@ __device__ __forceinline__ Rows rows_of(const BwdParams& p, int b, int h, int kv
 // dQ.
 
 template <int D>
-__global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2)))
+void bwd_dq_kernel(BwdParams p) {
   using KT = LTile<D, 64>;
   constexpr int BN = 64, KB = 2, KS = D / 16, DB = D / 32, PS = BN / 16;
   // K ring of two tiles at [0, 2 BYTES), V ring at [2 BYTES, 4 BYTES).
@@ -413,17 +414,20 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dq_kernel(BwdParams p) {
   }
   mfma_drain();
 
-  if (qvalid) {
-    uint16_t* op = p.dq + (head_q + qrow) * D + 4 * g;
+  // dQ goes to device memory through LDS (store_rows_bf16), each wave's 32
+  // rows in its own 64 D bytes of the K ring, which no wave reads after the
+  // last step's barrier (and whose copies that barrier has seen land).
+  {
+    uint2 w[D / 8];
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        uint2 w;
-        w.x = pack_bf16x2(acc[db][rr * 4 + 0] * p.scale, acc[db][rr * 4 + 1] * p.scale);
-        w.y = pack_bf16x2(acc[db][rr * 4 + 2] * p.scale, acc[db][rr * 4 + 3] * p.scale);
-        *reinterpret_cast<uint2*>(op + db * 32 + rr * 8) = w;
+        w[db * 4 + rr].x = pack_bf16x2(acc[db][rr * 4 + 0] * p.scale, acc[db][rr * 4 + 1] * p.scale);
+        w[db * 4 + rr].y = pack_bf16x2(acc[db][rr * 4 + 2] * p.scale, acc[db][rr * 4 + 3] * p.scale);
       }
+    const int row0 = q0 + wave * 32;
+    store_rows_bf16<D>(L + KRING + wave * 64 * D, w, lane_id(), p.dq + (head_q + row0) * D, Nq - row0);
   }
 }
 
@@ -709,39 +713,42 @@ __global__ __launch_bounds__(kThreads, 2) void bwd_dkdv_kernel(BwdParams p) {
   }
   mfma_drain();
 
-  // Lane (g, l32) holds key `key`, dims db*32 + 8 rr + 4 g + (0..3).
-  if (kvalid) {
-    if (p.G == 1) {
-      uint16_t* kp = p.dk + (head_kv + key) * D + 4 * g;
-      uint16_t* vp = p.dv + (head_kv + key) * D + 4 * g;
+  // Lane (g, l32) holds key `key`, dims db*32 + 8 rr + 4 g + (0..3). The
+  // results go to device memory through LDS (store_rows_bf16 / _f32), each
+  // wave's 32 keys in its own 128 D bytes of the V tile and the rings, which
+  // no wave reads after the last step's barrier (and whose copies that
+  // barrier has seen land); the fp32 partials pass through it one tensor
+  // after the other.
+  lds_u8* const region = L + wave * 128 * D;
+  const int row0 = k0 + wave * 32;
+  if (p.G == 1) {
+    uint2 wk[D / 8], wv[D / 8];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          uint2 wk, wv;
-          wk.x = pack_bf16x2(dka[db][rr * 4 + 0] * p.scale, dka[db][rr * 4 + 1] * p.scale);
-          wk.y = pack_bf16x2(dka[db][rr * 4 + 2] * p.scale, dka[db][rr * 4 + 3] * p.scale);
-          wv.x = pack_bf16x2(dva[db][rr * 4 + 0], dva[db][rr * 4 + 1]);
-          wv.y = pack_bf16x2(dva[db][rr * 4 + 2], dva[db][rr * 4 + 3]);
-          *reinterpret_cast<uint2*>(kp + db * 32 + rr * 8) = wk;
-          *reinterpret_cast<uint2*>(vp + db * 32 + rr * 8) = wv;
-        }
-    } else {
-      const size_t part = (R.head_p + key) * D + 4 * g;
-      float* kp = p.dk_part + part;
-      float* vp = p.dv_part + part;
+      for (int rr = 0; rr < 4; ++rr) {
+        const int c = db * 4 + rr;
+        wk[c].x = pack_bf16x2(dka[db][rr * 4 + 0] * p.scale, dka[db][rr * 4 + 1] * p.scale);
+        wk[c].y = pack_bf16x2(dka[db][rr * 4 + 2] * p.scale, dka[db][rr * 4 + 3] * p.scale);
+        wv[c].x = pack_bf16x2(dva[db][rr * 4 + 0], dva[db][rr * 4 + 1]);
+        wv[c].y = pack_bf16x2(dva[db][rr * 4 + 2], dva[db][rr * 4 + 3]);
+      }
+    store_rows_bf16<D>(region, wk, lane, p.dk + (head_kv + row0) * D, Nk - row0);
+    store_rows_bf16<D>(region + 64 * D, wv, lane, p.dv + (head_kv + row0) * D, Nk - row0);
+  } else {
+    f32x4 wk[D / 8], wv[D / 8];
 #pragma unroll
-      for (int db = 0; db < DB; ++db)
+    for (int db = 0; db < DB; ++db)
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const int r = rr * 4;
-          *reinterpret_cast<f32x4*>(kp + db * 32 + rr * 8) =
-              f32x4{dka[db][r] * p.scale, dka[db][r + 1] * p.scale, dka[db][r + 2] * p.scale,
-                    dka[db][r + 3] * p.scale};
-          *reinterpret_cast<f32x4*>(vp + db * 32 + rr * 8) =
-              f32x4{dva[db][r], dva[db][r + 1], dva[db][r + 2], dva[db][r + 3]};
-        }
-    }
+      for (int rr = 0; rr < 4; ++rr) {
+        const int r = rr * 4;
+        wk[db * 4 + rr] = f32x4{dka[db][r] * p.scale, dka[db][r + 1] * p.scale,
+                                dka[db][r + 2] * p.scale, dka[db][r + 3] * p.scale};
+        wv[db * 4 + rr] = f32x4{dva[db][r], dva[db][r + 1], dva[db][r + 2], dva[db][r + 3]};
+      }
+    const size_t part = (R.head_p + row0) * D;
+    store_rows_f32<D>(region, wk, lane, p.dk_part + part, Nk - row0);
+    store_rows_f32<D>(region, wv, lane, p.dv_part + part, Nk - row0);
   }
 }
 

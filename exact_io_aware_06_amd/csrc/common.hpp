@@ -220,6 +220,91 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
+// ---- Row stores through LDS -------------------------------------------------
+//
+// A wave's 32 x D block of matrix-core results has lane l holding values
+// 32 db + 8 rr + 4 (l / 32) .. + 4 of row l % 32 (db < D / 32, rr < 4).
+// Stored straight from the registers, each instruction writes short pieces of
+// 32 rows. These helpers move the block through a wave-private LDS region
+// first, so that each store to device memory moves 16 contiguous bytes per
+// lane and whole rows per instruction. In the region, row r sits at
+// r * (row bytes) with its 16-byte chunks permuted by an XOR of r's low bits
+// (for bf16 the two 8-byte halves of a chunk are also swapped when bit 4 of r
+// is set). That puts the pieces written by each group of 32 lanes (8-byte,
+// bf16) or 16 lanes (16-byte, fp32), and the chunks read by each group of 16
+// lanes, on distinct banks; the counters still show a few conflict cycles
+// per work-group, about 0.1 % of its time. The caller guarantees that no
+// other wave touches the region
+// until this wave is done with it. `out` is row 0 of the block; rows at or
+// past `nrows` are not stored.
+
+// This lane's index in its wave, from the lane counter (for code after a
+// loop that has no register to spare for keeping it).
+__device__ __forceinline__ int lane_id() {
+  return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Orders this wave's LDS accesses on either side. One wave's LDS operations
+// are performed in order, so this only keeps the compiler from moving them.
+__device__ __forceinline__ void region_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// bf16 rows of D elements (64 D bytes of LDS); w[4 db + rr] holds the lane's
+// four values as two packed pairs.
+template <int D>
+__device__ __forceinline__ void store_rows_bf16(lds_u8* region, const uint2 (&w)[D / 8], int lane,
+                                                uint16_t* out, int nrows) {
+  constexpr int ROWB = 2 * D, CPR = ROWB / 16, RPI = 64 / CPR;
+  auto fsw = [](int r) { return D == 128 ? (r & 15) : ((r >> 1) & 7); };
+  region_fence();  // after this wave's earlier reads of the region
+  {
+    const int r = lane & 31, g = lane >> 5;
+    const uint32_t rb = (uint32_t)(r * ROWB + 8 * ((g ^ (r >> 4)) & 1));
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) lds_st_b64(region, rb + (uint32_t)((c ^ fsw(r)) << 4), w[c]);
+  }
+  region_fence();  // each lane reads back what other lanes of its wave wrote
+  const int cl = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    const uint32_t at = (uint32_t)(r * ROWB + ((cl ^ fsw(r)) << 4));
+    const uint4 u = __builtin_bit_cast(uint4, lds_b128(region, at));
+    const bool hi_first = (i * RPI) & 16;  // bit 4 of r, the same for every lane here
+    const uint4 v = hi_first ? make_uint4(u.z, u.w, u.x, u.y) : u;
+    if (r < nrows) *reinterpret_cast<uint4*>(out + (size_t)r * D + cl * 8) = v;
+  }
+}
+
+// fp32 rows of D elements (128 D bytes of LDS); w[4 db + rr] holds the lane's
+// four values.
+template <int D>
+__device__ __forceinline__ void store_rows_f32(lds_u8* region, const f32x4 (&w)[D / 8], int lane,
+                                               float* out, int nrows) {
+  constexpr int ROWB = 4 * D, CPR = ROWB / 16, RPI = 64 / CPR;
+  region_fence();
+  {
+    const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+    for (int c = 0; c < D / 8; ++c) {
+      const int chunk = 2 * c + g;  // 16-byte chunk of values 4 chunk .. + 4
+      *(__attribute__((address_space(3))) f32x4*)(region + r * ROWB + ((chunk ^ (r & 15)) << 4)) =
+          w[c];
+    }
+  }
+  region_fence();
+  const int cl = lane % CPR;
+#pragma unroll
+  for (int i = 0; i < 32 / RPI; ++i) {
+    const int r = i * RPI + lane / CPR;
+    const f32x4 v =
+        *(const __attribute__((address_space(3))) f32x4*)(region + r * ROWB + ((cl ^ (r & 15)) << 4));
+    if (r < nrows) *reinterpret_cast<f32x4*>(out + (size_t)r * D + cl * 4) = v;
+  }
+}
+
 // Interleave the low halves (pick = 0) or high halves (pick = 1) of two
 // dwords holding bf16 pairs: result = {a.half, b.half}.
 __device__ __forceinline__ uint32_t interleave16(uint32_t a, uint32_t b, int pick) {

@@ -671,23 +671,29 @@ void fwd_bf16_kernel(FwdParams p) {
   const float inv = lb > 0.f ? 1.f / lb : 0.f;
   // This lane's row, recomputed from the lane counter rather than kept live
   // across the key loop (the loop has no register to spare for it).
-  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  const int lane_e = lane_id();
   const int ge = lane_e >> 5;
   const int qrow_e = q0 + wave * 32 + (lane_e & 31);
-  if (qrow_e < Nq) {
-    uint16_t* op = p.o + (head_q + qrow_e) * D + 4 * ge;
+  // O goes to device memory through LDS (store_rows_bf16), each wave's 32
+  // rows in its own 64 D bytes from offset 0. With bf16 K that is the K ring,
+  // which no wave reads after the last step's barrier (and whose copies that
+  // barrier has seen land); the fp8 K ring is smaller, so there the
+  // work-group first waits for every wave.
+  if constexpr (FP8) __syncthreads();
+  {
+    uint2 w[D / 8];
 #pragma unroll
     for (int db = 0; db < T::DB; ++db)
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr) {
-        uint2 w;
-        w.x = pack_bf16x2(oacc[db][rr * 4 + 0] * inv, oacc[db][rr * 4 + 1] * inv);
-        w.y = pack_bf16x2(oacc[db][rr * 4 + 2] * inv, oacc[db][rr * 4 + 3] * inv);
-        *reinterpret_cast<uint2*>(op + db * 32 + rr * 8) = w;
+        w[db * 4 + rr].x = pack_bf16x2(oacc[db][rr * 4 + 0] * inv, oacc[db][rr * 4 + 1] * inv);
+        w[db * 4 + rr].y = pack_bf16x2(oacc[db][rr * 4 + 2] * inv, oacc[db][rr * 4 + 3] * inv);
       }
-    if (ge == 0 && p.lse != nullptr)
-      p.lse[head_q + qrow_e] = lf > 0.f ? m_ref * p.scale + fast_log2(lf) * kLn2 : -kInf;
+    const int row0 = q0 + wave * 32;
+    store_rows_bf16<D>(L + wave * 64 * D, w, lane_e, p.o + (head_q + row0) * D, Nq - row0);
   }
+  if (qrow_e < Nq && ge == 0 && p.lse != nullptr)
+    p.lse[head_q + qrow_e] = lf > 0.f ? m_ref * p.scale + fast_log2(lf) * kLn2 : -kInf;
   if (COUNT && tid == 0) {
     int* c = p.counts + 2 * ((size_t)(b * p.H + h) * p.nqt + qt);
     c[0] = loaded;
