@@ -2,12 +2,14 @@
 
 With per-sequence cache lengths the decode does not cut each sequence into S
 equal chunks. It lays the visible keys of all sequences end to end in tiles of
-128 keys and hands each of its W work-groups per KV head (at most B * S; the
-launch caps W at one round of the work-groups the device holds at once) an
-equal run of whole tiles; a run that crosses a sequence boundary yields one partial result
-per sequence it touches, and the partial of (work-group w, sequence b) is
-stored as partial w + b. The merge finds a sequence's partials from the
-running tile counts alone.
+128 keys, each sequence that has keys preceded by PIECE virtual tiles (for
+what a piece costs beyond its tiles), and hands each of its W work-groups per
+KV head (at most B * S; the launch caps W at one round of the work-groups the
+device holds at once) an equal run of these units; a run that crosses a
+sequence boundary yields one partial result per sequence it touches (empty
+when the run holds only that sequence's virtual tiles), and the partial of
+(work-group w, sequence b) is stored as partial w + b. The merge finds a
+sequence's partials from the running unit counts alone.
 
 This test restates that plan in plain Python and checks the properties the
 kernels rely on, over random batches (empty sequences, one-key sequences,
@@ -28,6 +30,7 @@ import random
 import pytest
 
 TILE = 128
+PIECE = 1  # virtual tiles per sequence with keys
 
 
 def visible(n, Nk, window):
@@ -42,7 +45,8 @@ def plan(lens, Nk, window, W):
     T = [0]
     for n in lens:
         vis, hi = visible(n, Nk, window)
-        T.append(T[-1] + (hi - vis + TILE - 1) // TILE)
+        t = (hi - vis + TILE - 1) // TILE
+        T.append(T[-1] + (t + PIECE if t > 0 else 0))
     total = T[-1]
     budget = max(1, -(-total // W))
     first = {}
@@ -74,9 +78,11 @@ def run_plan(lens, Nk, window, S, W=None):
         assert T[b] <= g_lo < T[b + 1]
         while True:
             vis, n = visible(lens[b], Nk, window)
-            t_lo, t_hi = max(T[b], g_lo) - T[b], min(T[b + 1], g_hi) - T[b]
+            t_lo = max(0, max(T[b], g_lo) - T[b] - PIECE)
+            t_hi = max(0, min(T[b + 1], g_hi) - T[b] - PIECE)
             start, hi = vis + t_lo * TILE, min(n, vis + t_hi * TILE)
-            assert t_hi > t_lo and start < hi
+            # a piece is empty only when the run ends inside the virtual tiles
+            assert (t_hi > t_lo and start < hi) or (t_hi == t_lo == 0 and min(T[b + 1], g_hi) - T[b] <= PIECE)
             keys[b].extend(range(start, hi))
             idx = w + b
             assert idx not in written and idx < B * (S + 1)
@@ -113,12 +119,16 @@ def test_plan_covers_keys_once_with_unique_partials(seed):
         run_plan(lens, Nk, window, S, W=rng.randint(1, B * S))
 
 
-def test_plan_equal_full_lengths_are_the_equal_chunks():
-    """Equal lengths with chunks of whole tiles: the pieces are the equal chunks."""
+def test_plan_equal_full_lengths():
+    """Equal lengths: every work-group's run is budget units, so a sequence of 32
+    tiles and its virtual one (33 units) are spread over the 24 work-groups of three
+    sequences in runs of 5 units; the two runs that cross a boundary write two
+    partials each."""
     B, Nk, S = 3, 4096, 8
-    T, budget, _ = plan([Nk] * B, Nk, 0, B * S)
-    assert budget * TILE == Nk // S
-    assert run_plan([Nk] * B, Nk, 0, S) == B * S
+    T, budget, first = plan([Nk] * B, Nk, 0, B * S)
+    assert T == [0, 33, 66, 99] and budget == 5
+    assert sorted(first.items()) == [(w, (5 * w) // 33) for w in range(20)]
+    assert run_plan([Nk] * B, Nk, 0, S) == 20 + 2
 
 
 def test_plan_long_sequence_among_short_ones():
@@ -126,4 +136,7 @@ def test_plan_long_sequence_among_short_ones():
     lens = [20000] + [1] * 31
     T, budget, _ = plan(lens, 20000, 0, 32 * 16)
     assert budget == 1
-    assert run_plan(lens, 20000, 0, 16) == 157 + 31
+    # one work-group per unit: 157 tiles and a virtual one for the long sequence,
+    # a virtual and a real one for each one-key sequence
+    assert T[-1] == 158 + 31 * 2
+    assert run_plan(lens, 20000, 0, 16) == 158 + 31 * 2

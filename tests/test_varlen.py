@@ -292,16 +292,26 @@ def test_decode_varlen_ignores_rows_past_length():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
-@pytest.mark.parametrize("Nk,splits", [(777, 1), (1280, 5), (2048, 16), (4096, 8)])
+@pytest.mark.parametrize("Nk,splits", [(777, 1), (4000, 1), (1280, 5), (2048, 16), (4096, 8)])
 def test_decode_varlen_full_lengths_match_uniform_kernel(Nk, splits):
-    """All lengths equal to Nk, with each of the S equal chunks a whole number of 128-key
-    tiles (or one chunk per sequence): the balanced pieces of the per-sequence-length kernel
-    are then exactly the equal chunks, merged in the same order, so the two agree bit for bit."""
+    """All lengths equal to Nk. With one chunk per sequence the balanced plan gives each
+    work-group one whole sequence (its virtual tile and all its keys), the uniform kernel's
+    chunk, so the two agree bit for bit. With S chunks the plan's runs are shifted by one
+    virtual tile per sequence against the equal chunks: the same keys in other pieces. The
+    merge combines any partition exactly in exact arithmetic, but each piece rounds P to bf16
+    relative to its own reference maximum, which depends on where the piece starts, so here
+    both results are held to the oracle's bound instead of to each other."""
     q, kc, vc = decode_case(3, 32, 8, Nk, 128, seed=4)
     o1, l1 = run_decode(q, kc, vc, [Nk] * 3, 0.088, 0, splits)
     o2, l2 = mi.attn_decode(q.to(DEV), kc.to(DEV), vc.to(DEV), scale=0.088, num_splits=splits)
     torch.cuda.synchronize()
-    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    if splits == 1:
+        assert torch.equal(o1, o2) and torch.equal(l1, l2)
+        return
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, [Nk] * 3, 0.088, 0)
+    for o, lse, name in ((o1, l1, "per-sequence lengths"), (o2, l2, "equal chunks")):
+        check_out(to64(o), o_ref, label=f"{name} Nk={Nk} S={splits}")
+        check_lse(to64(lse), l_ref, label=f"{name} Nk={Nk} S={splits}")
 
 
 def test_decode_varlen_matches_one_query_packed_prefill():
