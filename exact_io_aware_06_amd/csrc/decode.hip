@@ -7,8 +7,10 @@
 // independent work. With equal lengths, each sequence's Nk cache rows are cut
 // into S contiguous chunks, and each (sequence, KV head, chunk) becomes one
 // work-group that reads its K/V rows exactly once for all G query heads
-// sharing that KV head. With per-sequence lengths, a small plan kernel lays
-// the visible keys of all sequences end to end in tiles, and each of the
+// sharing that KV head. With per-sequence lengths, a plan lays the visible
+// keys of all sequences end to end in tiles (computed by every split
+// work-group itself for up to 256 sequences, by a small plan kernel for
+// larger batches), and each of the
 // work-groups per KV head (at most B * S, and at most one round of the
 // work-groups the device holds at once) takes an equal run of whole tiles
 // (each sequence counted one tile longer, for what a piece costs beyond its
@@ -96,6 +98,12 @@ constexpr int kBN = 128;  // keys per tile: four waves x 32
 // [1, 2047] 0.0543 -> 0.0528 ms, equal and uniform-random lengths unchanged;
 // two virtual tiles gained less.
 constexpr int kPieceUnits = 1;
+// Batches of at most this many sequences (one per thread of a work-group) have
+// their plan computed by every split work-group itself, without the plan
+// kernel and its launch (same-process A/B, bit-identical: the skewed batch
+// 0.1906 -> 0.1869 ms, 64 random lengths in [1, 2047] 0.0528 -> 0.0495 ms,
+// the uniform random lengths of 32768-key slots 0.6606 -> 0.6572 ms).
+constexpr int kFoldMaxB = 256;
 constexpr float kRescaleThreshold = 8.0f;
 
 struct SplitParams {
@@ -109,11 +117,15 @@ struct SplitParams {
   int window;
   float scale, scale_log2, thr_raw;
   const int* kv_lens;  // per-sequence key counts, or null (all Nk)
-  // Balanced pieces (per-sequence lengths): the plan written by
-  // decode_plan_kernel, tcum[0..B] = running sum of the sequences' units
-  // (visible tiles plus kPieceUnits), tcum[B + 1] = units per work-group,
-  // tcum[B + 2 + w] = the sequence holding work-group w's first unit.
-  const int* tcum;
+  // Balanced pieces (per-sequence lengths): the plan, tcum[0..B] = running
+  // sum of the sequences' units (visible tiles plus kPieceUnits), tcum[B + 1]
+  // = units per work-group, tcum[B + 2 + w] = the sequence holding
+  // work-group w's first unit. decode_plan_kernel writes it and the split
+  // kernel reads it, or (FOLD, B <= kFoldMaxB) every split work-group
+  // computes tcum[0..B + 1] itself, for W work-groups per unit, and
+  // work-group 0 writes that much of it here for the merge.
+  int* tcum;
+  int W;
   // Paged cache: k, v are page pools [num_pages, Hkv, page_size, d] and
   // block_table [B, max_pages] names the physical page of each sequence's
   // j-th run of page_size keys (Nk = max_pages * page_size).
@@ -170,7 +182,7 @@ __device__ __forceinline__ int vswz(int r) {
   return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
 }
 
-template <int D, bool PAGED, bool BAL>
+template <int D, bool PAGED, bool BAL, bool FOLD = false>
 __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p) {
   using T = DTile<D>;
   __shared__ __attribute__((aligned(16))) uint16_t smem[T::STAGE];
@@ -211,11 +223,20 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
     vis = p.window > 0 ? max(0, n - 1 - p.window) : 0;
     return n;
   };
+  // Balanced pieces, folded plan: the running unit counts in LDS.
+  __shared__ int tc_lds[FOLD ? kFoldMaxB + 1 : 1];
+  __shared__ int fold_tmp[FOLD ? kThreads / 64 + 1 : 1];
+  // (LDS values are the same in every lane: readfirstlane keeps them, and the
+  // branches on them, scalar.)
+  auto cum = [&](int i) -> int {
+    if constexpr (FOLD) return __builtin_amdgcn_readfirstlane(tc_lds[i]);
+    return p.tcum[i];
+  };
   // BAL: the piece of sequence b inside [g_lo, g_hi).
   auto piece = [&]() {
     int vis;
     const int n = seq_keys(b, vis);
-    const int tb = p.tcum[b], tb1 = p.tcum[b + 1];
+    const int tb = cum(b), tb1 = cum(b + 1);
     // This share's units of the sequence, less its virtual tiles (a share
     // that holds only those gets an empty piece, whose partial weighs nothing).
     const int t_lo = max(0, max(tb, g_lo) - tb - kPieceUnits);
@@ -225,11 +246,58 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
     ntiles = t_hi - t_lo;
   };
   if constexpr (BAL) {
-    const int total = p.tcum[p.B], budget = p.tcum[p.B + 1];
-    g_lo = s * budget;
-    if (g_lo >= total) return;  // the batch's tiles are all taken by earlier work-groups
+    int total, budget;
+    if constexpr (FOLD) {
+      // The plan of decode_plan_kernel, for B <= kThreads: thread b holds
+      // sequence b's units; an inclusive scan over the work-group gives the
+      // running counts.
+      int t = 0;
+      if (tid < p.B) {
+        int vis;
+        const int n = seq_keys(tid, vis);
+        t = (n - vis + kBN - 1) / kBN;
+        t = t > 0 ? t + kPieceUnits : 0;
+      }
+      int x = t;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+      }
+      if (lane == 63) fold_tmp[wave] = x;
+      __syncthreads();
+      int before = 0;
+      total = 0;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) {
+        before += w < wave ? fold_tmp[w] : 0;
+        total += fold_tmp[w];
+      }
+      total = __builtin_amdgcn_readfirstlane(total);
+      if (tid < p.B) tc_lds[tid + 1] = before + x;
+      if (tid == 0) tc_lds[0] = 0;
+      budget = max(1, (total + p.W - 1) / p.W);
+      __syncthreads();
+      // The merge reads the running counts and the budget; work-group 0
+      // publishes them (also when every sequence is empty).
+      if (blockIdx.x == 0) {
+        for (int i = tid; i <= p.B; i += kThreads) p.tcum[i] = tc_lds[i];
+        if (tid == 0) p.tcum[p.B + 1] = budget;
+      }
+      g_lo = s * budget;
+      if (g_lo >= total) return;  // the batch's units are all taken by earlier work-groups
+      // The sequence that owns unit g_lo (exactly one, since g_lo < total).
+      if (tid < p.B && tc_lds[tid] <= g_lo && g_lo < tc_lds[tid + 1]) fold_tmp[kThreads / 64] = tid;
+      __syncthreads();
+      b = __builtin_amdgcn_readfirstlane(fold_tmp[kThreads / 64]);
+    } else {
+      total = p.tcum[p.B];
+      budget = p.tcum[p.B + 1];
+      g_lo = s * budget;
+      if (g_lo >= total) return;  // the batch's units are all taken by earlier work-groups
+      b = p.tcum[p.B + 2 + s];    // the sequence that owns unit g_lo
+    }
     g_hi = min(total, g_lo + budget);
-    b = p.tcum[p.B + 2 + s];    // the sequence that owns tile g_lo
     piece();
   } else {
     b = bk / p.Hkv;
@@ -461,11 +529,11 @@ __global__ __launch_bounds__(kThreads, 2) void decode_split_kernel(SplitParams p
     if constexpr (!BAL) {
       break;
     } else {
-      if (p.tcum[b + 1] >= g_hi) break;
-      // The next sequence that owns tiles (one does: this share goes on).
+      if (cum(b + 1) >= g_hi) break;
+      // The next sequence that owns units (one does: this share goes on).
       do {
         ++b;
-      } while (p.tcum[b + 1] == p.tcum[b]);
+      } while (cum(b + 1) == cum(b));
       piece();
       load_q();
     }
@@ -615,6 +683,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   // balanced pieces; equal lengths keep one equal chunk per work-group.
   const bool bal = a.kv_lens != nullptr;
   sp.tcum = bal ? plan : nullptr;
+  const bool fold = bal && a.B <= kFoldMaxB;
   sp.B = a.B;
   sp.H = a.H;
   sp.Hkv = a.Hkv;
@@ -635,12 +704,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
   const bool paged = a.block_table != nullptr;
   const void* sfn;
   if (a.d == 128)
-    sfn = paged ? reinterpret_cast<const void*>(&decode_split_kernel<128, true, true>)
-          : bal ? reinterpret_cast<const void*>(&decode_split_kernel<128, false, true>)
+    sfn = paged ? (fold ? reinterpret_cast<const void*>(&decode_split_kernel<128, true, true, true>)
+                        : reinterpret_cast<const void*>(&decode_split_kernel<128, true, true>))
+          : bal ? (fold ? reinterpret_cast<const void*>(&decode_split_kernel<128, false, true, true>)
+                        : reinterpret_cast<const void*>(&decode_split_kernel<128, false, true>))
                 : reinterpret_cast<const void*>(&decode_split_kernel<128, false, false>);
   else
-    sfn = paged ? reinterpret_cast<const void*>(&decode_split_kernel<64, true, true>)
-          : bal ? reinterpret_cast<const void*>(&decode_split_kernel<64, false, true>)
+    sfn = paged ? (fold ? reinterpret_cast<const void*>(&decode_split_kernel<64, true, true, true>)
+                        : reinterpret_cast<const void*>(&decode_split_kernel<64, true, true>))
+          : bal ? (fold ? reinterpret_cast<const void*>(&decode_split_kernel<64, false, true, true>)
+                        : reinterpret_cast<const void*>(&decode_split_kernel<64, false, true>))
                 : reinterpret_cast<const void*>(&decode_split_kernel<64, false, false>);
   // Equal chunks: B * S work-groups per (KV head, head block). Balanced
   // pieces: at most B * S, and no more than one round of the work-groups the
@@ -668,7 +741,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
             "merge_grid=%d\n",
             a.d, a.splits, bal ? "per-sequence (balanced pieces)" : "uniform",
             a.block_table != nullptr ? a.page_size : 0, nsplit_blk, a.B * a.H);
-  if (bal) {
+  sp.W = (int)per_unit;
+  if (bal && !fold) {
     PlanParams pp{a.kv_lens, plan, a.B, a.Nk, a.window, (int)per_unit};
     void* pargs[] = {&pp};
     e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_plan_kernel), dim3(1),

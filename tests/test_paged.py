@@ -73,6 +73,19 @@ def test_paged_many_heads_per_group(H, Hkv):
     check_lse(to64(lse), l_ref, label=f"H={H} Hkv={Hkv}")
 
 
+@pytest.mark.parametrize("B", [256, 300])
+def test_paged_large_batches(B):
+    """Both ways of planning the balanced pieces (in the split work-groups up to 256
+    sequences, by a plan kernel past that) over a paged cache."""
+    r = np.random.default_rng(B + 1)
+    lens = [int(x) for x in r.choice([0, 1, 16, 40, int(r.integers(0, 200))], B)]
+    q, kp, vp, table = paged_case(lens, 16, 4, 2, 64, seed=B)
+    o, lse = run_paged(q, kp, vp, table, lens, 0.125, 0, 2)
+    o_ref, l_ref = oracle.decode_paged_ref(q, kp, vp, table, lens, 16, 0.125, 0)
+    check_out(to64(o), o_ref, label=f"B={B}")
+    check_lse(to64(lse), l_ref, label=f"B={B}")
+
+
 @pytest.mark.parametrize("ps,splits", [(16, 1), (16, 8), (64, 5), (128, 16)])
 def test_paged_matches_contiguous_decode(ps, splits):
     """Same keys, same chunks: identical to the contiguous mixed-length decode."""

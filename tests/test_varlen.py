@@ -314,6 +314,23 @@ def test_decode_varlen_full_lengths_match_uniform_kernel(Nk, splits):
         check_lse(to64(lse), l_ref, label=f"{name} Nk={Nk} S={splits}")
 
 
+@pytest.mark.parametrize("B", [256, 257, 300])
+def test_decode_varlen_large_batches(B):
+    """Up to 256 sequences every split work-group plans its own run of tiles; past that a
+    separate plan kernel writes the plan first. Both sides of the boundary, with empty,
+    one-key and ragged sequences, against the oracle."""
+    r = np.random.default_rng(B)
+    lens = [int(x) for x in r.choice([0, 1, 64, 129, int(r.integers(0, 300))], B)]
+    lens[-1] = 300  # a full sequence at the end of the batch
+    q, kc, vc = decode_case(B, 4, 2, 300, 64, seed=B)
+    o, lse = run_decode(q, kc, vc, lens, 0.125, 0, 3)
+    o_ref, l_ref = oracle.decode_kvlens_ref(q, kc, vc, lens, 0.125, 0)
+    check_out(to64(o), o_ref, label=f"B={B}")
+    check_lse(to64(lse), l_ref, label=f"B={B}")
+    empty = [b for b, n in enumerate(lens) if n == 0]
+    assert torch.all(o[empty] == 0) and torch.all(torch.isneginf(lse[empty]))
+
+
 def test_decode_varlen_matches_one_query_packed_prefill():
     """Sequence b is a one-query document over its kv_lens[b] keys."""
     lens = [1, 90, 300, 129]
