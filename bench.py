@@ -165,7 +165,7 @@ def write_traffic(fetch_csv: str, write_csv: str, skip: int, copy_mib: int) -> d
     want = {
         "fwd_bf16": (("fwd_bf16_kernel<128, false, false, true>", cp.B * cp.H * (cp.Nq // 128)),
                      accounting.prefill_bytes(cp.B, cp.H, cp.Hkv, cp.Nq, cp.Nk, cp.d)),
-        "decode": (("decode_split_kernel<128, false, false>", cd.B * cd.Hkv * cd.splits),
+        "decode": (("decode_split_kernel<128, false, false, false>", cd.B * cd.Hkv * cd.splits),
                    accounting.decode_bytes(cd.B, cd.H, cd.Hkv, cd.Nk, cd.d)),
     }
     out = {}
@@ -594,7 +594,7 @@ def main():
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic_for("fwd_bf16")},
         "ceilings": ceilings,
-        "roofline_decode": {"kernel": "decode_split_kernel<128, false, false> + decode_merge_kernel<128>",
+        "roofline_decode": {"kernel": "decode_split_kernel<128, false, false, false> + decode_merge_kernel<128>",
                             "bound": "hbm", "achieved": round(dec_gbs, 1),
                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
                             "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
